@@ -1,0 +1,200 @@
+"""Checkpoint + ring + cursor model of ReplaySSM, stepwise in float64 (oracle).
+
+TEST INFRASTRUCTURE ONLY.  Pages: page 4 "What shipped" (window of L buffered
+records, flush on a full buffer, drafts appended and the accepted prefix
+committed by advancing a pointer, records past the pointer ignored and
+overwritten); page 1, section on what the method does (flush writes the state
+once and empties the buffer) and section on what got faster (speculative
+drafts appended to the buffer; the pointer advances by the accepted count; a
+low-precision copy serves reads and never re-enters the recurrence).
+
+The oracle keeps the *conventional* state S at the committed position (the
+plain definition of what every output must equal) plus the integer cursor:
+
+* decode: the record goes to ring slot ``n_committed % C``; S advances one
+  step; ``n_committed += 1``; if ``h = n_committed - n_ckpt >= L`` the step is a
+  flush step: the checkpoint becomes S and ``n_ckpt = n_committed``.  The output
+  is ``S_t q_t`` (post-update state).  Reading: the flush happens on the step
+  that appends the L-th record, so 64 steps with L = 16 flush exactly 4 times.
+* verify(T): draft tau goes to slot ``(n_committed + tau) % C``; the counters do
+  not move; output tau is the stepwise recurrence over drafts 0..tau applied to
+  a temporary copy of S, which is then discarded.  Requires ``h + T <= C``.
+* commit(a): ``0 <= a <= T`` and ``h + a <= C``; the first ``a`` drafts advance S
+  stepwise; ``n_committed += a``.  Nothing else.
+* flush(min_records): sequences with ``h >= max(min_records, 1)`` make the
+  checkpoint equal S and set ``n_ckpt = n_committed``.
+* read copy (decode only): at init and at every flush the float32 checkpoint
+  is quantised; a second stepwise chain R restarts from the dequantised copy.
+  Non-flush outputs are ``R_t q_t``; flush-step outputs come from S.  R never
+  feeds S.
+
+A contract violation (verify with ``h + T > C``, commit with ``a`` out of range)
+leaves that sequence untouched and sets the sticky error flag; its outputs are
+NaN here.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from .recurrence import widen, step
+from .quant import read_copy_dequant
+
+
+class OracleError(ValueError):
+    pass
+
+
+_FIELDS = ("alpha", "beta", "v", "k", "q")
+
+
+class ReplayOracle:
+    """Oracle over the sequences ``seqs`` of workload ``wl``.
+
+    ``S0``: float32 [len(seqs), H, P, N] or None (zeros).  With
+    ``track_state=False`` only the integer cursor policy runs (cheap, for checking
+    counters of a whole batch).
+    """
+
+    def __init__(self, wl, seqs: Sequence[int], S0: Optional[np.ndarray] = None,
+                 track_state: bool = True):
+        if wl.n_heads % wl.n_qk_heads:
+            raise OracleError("H % G != 0")
+        if wl.capacity < wl.L + wl.t_max - 1:
+            raise OracleError("capacity < L + t_max - 1")
+        self.wl = wl
+        self.seqs = list(seqs)
+        nb = len(self.seqs)
+        self.n_committed = np.zeros(nb, np.int64)
+        self.n_ckpt = np.zeros(nb, np.int64)
+        self.err = False
+        self.track_state = track_state
+        self.flush_count = np.zeros(nb, np.int64)
+        H, G, P, N, C = wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk, wl.capacity
+        dt = np.float32 if wl.in_dtype == "fp32" else np.uint16
+        # ring of raw stored inputs (bit-exact copies of what was appended)
+        self.ring = {
+            "alpha": np.zeros((nb, C, H), dt),
+            "beta": np.zeros((nb, C, H), dt),
+            "v": np.zeros((nb, C, H, P), dt),
+            "k": np.zeros((nb, C, G, N), dt),
+            "q": np.zeros((nb, C, G, N), dt),
+        }
+        self._drafts = None
+        self._drafts_T = 0
+        if track_state:
+            if S0 is None:
+                S0 = np.zeros((nb, H, P, N), np.float32)
+            if S0.dtype != np.float32 or S0.shape != (nb, H, P, N):
+                raise OracleError("S0 must be float32 [nb, H, P, N]")
+            self.S = S0.astype(np.float64)
+            self.S_ckpt = self.S.copy()
+            self.R = None
+            if wl.read_copy != "none":
+                self.R = read_copy_dequant(wl.read_copy, S0.astype(np.float32))
+
+    # -- helpers ---------------------------------------------------------------
+    def h(self) -> np.ndarray:
+        return self.n_committed - self.n_ckpt
+
+    def _rec(self, inp: Dict[str, Optional[np.ndarray]], i: int, t: Optional[int] = None):
+        out = {}
+        for f in _FIELDS:
+            a = inp.get(f)
+            if a is None:
+                out[f] = None
+                continue
+            a = a[i] if t is None else a[i, t]
+            out[f] = widen(a, self.wl.in_dtype)
+        return out
+
+    def _store(self, i: int, slot: int, inp, t: Optional[int] = None):
+        for f in _FIELDS:
+            a = inp.get(f)
+            if a is None:
+                continue
+            self.ring[f][i, slot] = a[i] if t is None else a[i, t]
+
+    def _checkpoint(self, i: int):
+        self.S_ckpt[i] = self.S[i]
+        if self.R is not None:
+            self.R[i] = read_copy_dequant(self.wl.read_copy, self.S[i].astype(np.float32))
+
+    # -- operations ------------------------------------------------------------
+    def decode(self, inp) -> np.ndarray:
+        """One decode step; ``inp`` arrays have leading dim len(seqs).  Returns y [nb,H,P]."""
+        wl = self.wl
+        nb = len(self.seqs)
+        y = np.full((nb, wl.n_heads, wl.dv), np.nan)
+        for i in range(nb):
+            slot = int(self.n_committed[i] % wl.capacity)
+            self._store(i, slot, inp)
+            self.n_committed[i] += 1
+            flush = self.n_committed[i] - self.n_ckpt[i] >= wl.L
+            if self.track_state:
+                rec = self._rec(inp, i)
+                self.S[i], y_full = step(wl.kind, self.S[i], rec)
+                if self.R is not None and not flush:
+                    self.R[i], y[i] = step(wl.kind, self.R[i], rec)
+                else:
+                    y[i] = y_full
+            if flush:
+                self.n_ckpt[i] = self.n_committed[i]
+                self.flush_count[i] += 1
+                if self.track_state:
+                    self._checkpoint(i)
+        return y
+
+    def verify(self, drafts, T: int) -> np.ndarray:
+        """Append T drafts past the cursor; return outputs [nb, T, H, P] (state untouched)."""
+        wl = self.wl
+        if not 1 <= T <= wl.t_max:
+            raise OracleError("T out of range")
+        nb = len(self.seqs)
+        O = np.full((nb, T, wl.n_heads, wl.dv), np.nan)
+        self._drafts, self._drafts_T = drafts, T
+        self._draft_ok = np.ones(nb, bool)
+        for i in range(nb):
+            if self.n_committed[i] - self.n_ckpt[i] + T > wl.capacity:
+                self.err = True
+                self._draft_ok[i] = False
+                continue
+            for t in range(T):
+                self._store(i, int((self.n_committed[i] + t) % wl.capacity), drafts, t)
+            if self.track_state:
+                S_tmp = self.S[i].copy()
+                for t in range(T):
+                    S_tmp, O[i, t] = step(wl.kind, S_tmp, self._rec(drafts, i, t))
+        return O
+
+    def commit(self, accept: np.ndarray, T: int):
+        """Advance the cursor by the accepted prefix length ``accept[i]`` (0..T)."""
+        wl = self.wl
+        if self._drafts is None:
+            raise OracleError("commit without a preceding verify")
+        for i in range(len(self.seqs)):
+            a = int(accept[i])
+            h = self.n_committed[i] - self.n_ckpt[i]
+            if a < 0 or a > T or h + a > wl.capacity or not self._draft_ok[i]:
+                self.err = True
+                continue
+            if self.track_state:
+                for t in range(a):
+                    self.S[i], _ = step(wl.kind, self.S[i], self._rec(self._drafts, i, t))
+            self.n_committed[i] += a
+
+    def flush(self, min_records: int):
+        """Fold sequences holding at least max(min_records, 1) records."""
+        thr = max(int(min_records), 1)
+        for i in range(len(self.seqs)):
+            if self.n_committed[i] - self.n_ckpt[i] >= thr:
+                self.n_ckpt[i] = self.n_committed[i]
+                self.flush_count[i] += 1
+                if self.track_state:
+                    self._checkpoint(i)
+
+    def live_slots(self, i: int):
+        """Ring slots holding the committed records since the checkpoint, oldest first."""
+        C = self.wl.capacity
+        return [int((self.n_ckpt[i] + j) % C) for j in range(int(self.n_committed[i] - self.n_ckpt[i]))]
