@@ -1,0 +1,56 @@
+// Gated DeltaNet instances of the decode, verify, flush and conventional kernels.
+#include "rssm_device.hpp"
+
+namespace rssm {
+
+namespace {
+constexpr int kKind = RSSM_KIND_GDN;
+
+inline dim3 grid_of(const Args &a) { return dim3((unsigned)(a.g.B * a.g.H)); }
+}  // namespace
+
+hipError_t launch_decode_gdn(const Args &a, hipStream_t s) {
+  const size_t lds = lds_bytes(kKind, a.g.C + 1, 1, a.g.P, a.g.N);
+#define CALL(n, r)                                                                          \
+  {                                                                                         \
+    hipLaunchKernelGGL((k_decode<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);     \
+    return hipGetLastError();                                                               \
+  }
+  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+#undef CALL
+}
+
+hipError_t launch_verify_gdn(const Args &a, hipStream_t s) {
+  const size_t lds = lds_bytes(kKind, a.g.C, a.T, a.g.P, a.g.N);
+#define CALL(n, r)                                                                          \
+  {                                                                                         \
+    hipLaunchKernelGGL((k_verify<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);     \
+    return hipGetLastError();                                                               \
+  }
+  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+#undef CALL
+}
+
+hipError_t launch_flush_gdn(const Args &a, hipStream_t s) {
+  const size_t lds = lds_bytes(kKind, a.g.C, 1, a.g.P, a.g.N);
+#define CALL(n, r)                                                                          \
+  {                                                                                         \
+    hipLaunchKernelGGL((k_flush<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);      \
+    return hipGetLastError();                                                               \
+  }
+  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+#undef CALL
+}
+
+hipError_t launch_conventional_gdn(const Args &a, hipStream_t s) {
+  const size_t lds = lds_bytes(kKind, 1, 1, a.g.P, a.g.N);
+#define CALL(n, r)                                                                          \
+  {                                                                                         \
+    hipLaunchKernelGGL((k_conventional<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a); \
+    return hipGetLastError();                                                               \
+  }
+  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+#undef CALL
+}
+
+}  // namespace rssm

@@ -1,0 +1,285 @@
+// Host layer of the C ABI (include/rssm.h): argument validation, buffer sizing,
+// geometry setup and kernel launch.  Nothing is enqueued when validation fails.
+#include <string.h>
+
+#include "rssm_internal.hpp"
+
+using namespace rssm;
+
+namespace {
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+bool dk_ok(int dk) { return dk == 32 || dk == 64 || dk == 128 || dk == 256; }
+
+int check_cfg(const rssm_config *c) {
+  if (!c) return RSSM_E_NULL;
+  if (c->kind != RSSM_KIND_MAMBA2 && c->kind != RSSM_KIND_GDN) return RSSM_E_DTYPE;
+  if (c->in_dtype != RSSM_DTYPE_F32 && c->in_dtype != RSSM_DTYPE_BF16) return RSSM_E_DTYPE;
+  if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_MXFP4) return RSSM_E_DTYPE;
+  if (c->batch < 0 || c->n_heads < 1 || c->n_qk_heads < 1) return RSSM_E_SHAPE;
+  if (c->n_heads % c->n_qk_heads) return RSSM_E_SHAPE;
+  if (!dk_ok(c->dk)) return RSSM_E_SHAPE;
+  if (c->dv < 1 || c->dv > 16384 / c->dk) return RSSM_E_SHAPE;
+  if (c->L < 1 || c->t_max < 1 || c->t_max > kMaxDrafts) return RSSM_E_RANGE;
+  if (c->capacity < c->L + c->t_max - 1 || c->capacity > kMaxCapacity) return RSSM_E_SHAPE;
+  if ((int64_t)c->batch * c->n_heads > (int64_t)(1 << 30)) return RSSM_E_SHAPE;
+  if (lds_bytes(c->kind, c->capacity + 1, 1, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
+  if (lds_bytes(c->kind, c->capacity, c->t_max, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
+  return RSSM_OK;
+}
+
+void ring_layout(const rssm_config *c, int64_t off[5], int64_t *total) {
+  const int64_t es = c->in_dtype == RSSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t B = c->batch, H = c->n_heads, G = c->n_qk_heads, C = c->capacity;
+  const int64_t P = c->dv, N = c->dk;
+  int64_t o = 0;
+  off[0] = o;                                   // alpha [B][H][C]
+  o = align256(o + B * H * C * es);
+  off[1] = o;                                   // beta [B][H][C] (GDN only)
+  if (c->kind == RSSM_KIND_GDN) o = align256(o + B * H * C * es);
+  off[2] = o;                                   // v [B][H][C][P]
+  o = align256(o + B * H * C * P * es);
+  off[3] = o;                                   // k [B][G][C][N]
+  o = align256(o + B * G * C * N * es);
+  off[4] = o;                                   // q [B][G][C][N]
+  o = align256(o + B * G * C * N * es);
+  *total = o;
+}
+
+Geom make_geom(const rssm_config *c) {
+  Geom g;
+  g.kind = c->kind;
+  g.B = c->batch;
+  g.H = c->n_heads;
+  g.G = c->n_qk_heads;
+  g.grp = c->n_heads / c->n_qk_heads;
+  g.P = c->dv;
+  g.N = c->dk;
+  g.L = c->L;
+  g.C = c->capacity;
+  g.bf16 = c->in_dtype == RSSM_DTYPE_BF16;
+  g.read_copy = c->read_copy;
+  int64_t off[5], total;
+  ring_layout(c, off, &total);
+  g.off_alpha = off[0];
+  g.off_beta = off[1];
+  g.off_v = off[2];
+  g.off_k = off[3];
+  g.off_q = off[4];
+  return g;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_state(const rssm_config *c, const rssm_state *st, bool need_ring) {
+  if (!st || !st->s_ckpt || !st->n_committed || !st->n_ckpt || !st->err) return RSSM_E_NULL;
+  if (need_ring && !st->ring) return RSSM_E_NULL;
+  if (c->read_copy != RSSM_READ_NONE && (!st->s_read || !st->s_read_scale)) return RSSM_E_NULL;
+  if (!aligned(st->s_ckpt, 16) || !aligned(st->n_committed, 8) || !aligned(st->n_ckpt, 8) || !aligned(st->err, 4))
+    return RSSM_E_ALIGN;
+  if (c->read_copy != RSSM_READ_NONE && (!aligned(st->s_read, 16) || !aligned(st->s_read_scale, 4)))
+    return RSSM_E_ALIGN;
+  if (need_ring && !aligned(st->ring, 256)) return RSSM_E_ALIGN;
+  return RSSM_OK;
+}
+
+int check_inputs(const rssm_config *c, const void *alpha, const void *beta, const void *v, const void *k,
+                 const void *q, const float *out) {
+  if (!alpha || !v || !k || !q || !out) return RSSM_E_NULL;
+  if (c->kind == RSSM_KIND_GDN && !beta) return RSSM_E_NULL;
+  const uintptr_t es = c->in_dtype == RSSM_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(alpha, es) || !aligned(v, es) || !aligned(k, es) || !aligned(q, es) || !aligned(out, 4))
+    return RSSM_E_ALIGN;
+  if (beta && !aligned(beta, es)) return RSSM_E_ALIGN;
+  return RSSM_OK;
+}
+
+Args make_args(const rssm_config *c, const rssm_state *st) {
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geom(c);
+  if (st) {
+    a.s = st->s_ckpt;
+    a.s_read = (uint8_t *)st->s_read;
+    a.s_read_scale = (uint8_t *)st->s_read_scale;
+    a.ring = (uint8_t *)st->ring;
+    a.n_committed = st->n_committed;
+    a.n_ckpt = st->n_ckpt;
+    a.err = st->err;
+  }
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int rssm_check_config(const rssm_config *cfg) { return check_cfg(cfg); }
+
+int rssm_sizes(const rssm_config *cfg, rssm_buffer_sizes *out) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if (!out) return RSSM_E_NULL;
+  const size_t tiles = (size_t)cfg->batch * cfg->n_heads;
+  const size_t PN = (size_t)cfg->dv * cfg->dk;
+  out->s_ckpt = tiles * PN * sizeof(float);
+  out->s_read = cfg->read_copy == RSSM_READ_FP8 ? tiles * PN : cfg->read_copy == RSSM_READ_MXFP4 ? tiles * PN / 2 : 0;
+  out->s_read_scale = cfg->read_copy == RSSM_READ_FP8     ? tiles * (PN / 32) * sizeof(float)
+                      : cfg->read_copy == RSSM_READ_MXFP4 ? tiles * (PN / 32)
+                                                          : 0;
+  int64_t off[5], total;
+  ring_layout(cfg, off, &total);
+  out->ring = (size_t)total;
+  out->n_committed = tiles * sizeof(int64_t);
+  out->n_ckpt = tiles * sizeof(int64_t);
+  out->err = sizeof(int32_t);
+  return RSSM_OK;
+}
+
+int rssm_ring_offsets(const rssm_config *cfg, int64_t *out5) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if (!out5) return RSSM_E_NULL;
+  int64_t total;
+  ring_layout(cfg, out5, &total);
+  return RSSM_OK;
+}
+
+int rssm_init_state(const rssm_config *cfg, const rssm_state *st, const float *s0, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, false))) return r;
+  if (s0 && !aligned(s0, 16)) return RSSM_E_ALIGN;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return RSSM_E_DEVICE;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return RSSM_E_DEVICE;
+  if (cfg->batch == 0) return hip_status(launch_clear_err(st->err, stream));
+  Args a = make_args(cfg, st);
+  a.s0 = s0;
+  return hip_status(launch_init(a, stream));
+}
+
+int rssm_decode_step(const rssm_config *cfg, const rssm_state *st, const void *alpha, const void *beta,
+                     const void *v, const void *k, const void *q, float *y, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, y))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = y;
+  return hip_status(launch_decode(a, stream));
+}
+
+int rssm_flush(const rssm_config *cfg, const rssm_state *st, int32_t min_records, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if (min_records < 0) return RSSM_E_RANGE;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.min_records = min_records;
+  return hip_status(launch_flush(a, stream));
+}
+
+int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const void *alpha, const void *beta,
+                const void *v, const void *k, const void *q, float *o, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, o))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = o;
+  a.T = T;
+  return hip_status(launch_verify(a, stream));
+}
+
+int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_accept, int32_t T,
+                hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, false))) return r;
+  if (!n_accept) return RSSM_E_NULL;
+  if (!aligned(n_accept, 4)) return RSSM_E_ALIGN;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.n_accept = n_accept;
+  a.T = T;
+  return hip_status(launch_commit(a, stream));
+}
+
+int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *alpha, const void *beta,
+                                  const void *v, const void *k, const void *q, float *y, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if (!s) return RSSM_E_NULL;
+  if (!aligned(s, 16)) return RSSM_E_ALIGN;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, y))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, nullptr);
+  a.s = s;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = y;
+  return hip_status(launch_conventional(a, stream));
+}
+
+int rssm_get_error(const rssm_state *st, hipStream_t stream) {
+  if (!st || !st->err) return RSSM_E_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return RSSM_E_HIP;
+  int32_t h = 0;
+  if (hipMemcpy(&h, st->err, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return RSSM_E_HIP;
+  if (launch_clear_err(st->err, stream) != hipSuccess) return RSSM_E_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return RSSM_E_HIP;
+  return h;
+}
+
+int rssm_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+  if (!src || !dst) return RSSM_E_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16) || bytes % 16) return RSSM_E_ALIGN;
+  return hip_status(launch_stream_copy(src, dst, bytes, stream));
+}
+
+const char *rssm_strerror(int code) {
+  switch (code) {
+    case RSSM_OK: return "ok";
+    case RSSM_E_NULL: return "a required pointer is NULL";
+    case RSSM_E_SHAPE: return "unsupported or inconsistent sizes";
+    case RSSM_E_DTYPE: return "unknown kind, input dtype or read-copy format";
+    case RSSM_E_ALIGN: return "misaligned pointer or size";
+    case RSSM_E_RANGE: return "argument out of range";
+    case RSSM_E_HIP: return "HIP runtime call failed";
+    case RSSM_E_DEVICE: return "no usable gfx950 device";
+    default: break;
+  }
+  if (code > 0) {
+    if (code & RSSM_DEVERR_CURSOR) return "device: inconsistent cursor counters";
+    if (code & RSSM_DEVERR_VERIFY_CAPACITY) return "device: verify would overflow the ring (h + T > capacity)";
+    if (code & RSSM_DEVERR_ACCEPT_RANGE) return "device: accepted count out of range";
+  }
+  return "unknown error";
+}
+
+int rssm_version(void) { return 100; }
+
+}  // extern "C"

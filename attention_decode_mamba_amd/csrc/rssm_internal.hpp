@@ -1,0 +1,105 @@
+// Internal definitions shared by the host layer (rssm_api.cpp) and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/rssm.h"
+
+namespace rssm {
+
+constexpr int kThreads = 256;   // 4 waves of 64 per workgroup
+constexpr int kWaves = 4;
+constexpr int kMaxCapacity = 32;
+constexpr int kMaxDrafts = 8;
+constexpr int kMaxLdsBytes = 64 * 1024;
+
+// Everything a kernel needs to address one (sequence, value-head) tile.
+struct Geom {
+  int kind;        // RSSM_KIND_*
+  int B, H, G, grp;
+  int P, N;        // tile rows (dv) and columns (dk)
+  int L, C;
+  int bf16;        // inputs and ring are raw bf16 bits
+  int read_copy;   // RSSM_READ_*
+  int64_t off_alpha, off_beta, off_v, off_k, off_q;   // byte offsets inside the ring
+};
+
+struct Args {
+  Geom g;
+  float *s;                 // S_ckpt, or the conventional state
+  uint8_t *s_read;
+  uint8_t *s_read_scale;
+  uint8_t *ring;
+  int64_t *n_committed;
+  int64_t *n_ckpt;
+  int32_t *err;
+  const void *alpha, *beta, *v, *k, *q;   // step or draft inputs
+  float *out;                              // y [B][H][P] or O [B][T][H][P]
+  const float *s0;                         // init source (may be null)
+  const int32_t *n_accept;                 // commit
+  int T;                                   // drafts (verify / commit)
+  int min_records;                         // flush threshold
+};
+
+// Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
+struct LdsLayout {
+  int alpha, beta, dec, coef, cc, gam, misc, q, r, K, V, gram, total;
+};
+
+__host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
+
+__host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P, int N) {
+  LdsLayout l;
+  int o = 0;
+  l.alpha = o; o += up4(cap);
+  l.beta = o;  o += up4(cap);
+  l.dec = o;   o += up4(cap);
+  l.coef = o;  o += up4(T * cap);
+  l.cc = o;    o += up4(T * cap);
+  l.gam = o;   o += up4(T);
+  l.misc = o;  o += 4;
+  l.q = o;     o += T * N;
+  l.r = o;     o += T * N;
+  l.K = o;     o += cap * (N + 4);
+  l.V = o;     o += up4(cap * P);
+  l.gram = o;  o += (kind == RSSM_KIND_GDN) ? up4(cap * (cap + 1)) : 0;
+  l.total = o;
+  return l;
+}
+
+inline size_t lds_bytes(int kind, int cap, int T, int P, int N) {
+  return (size_t)lds_layout(kind, cap, T, P, N).total * sizeof(float);
+}
+
+// Rows of a tile handled per wave: row blocks of 16, distributed over 4 waves.
+inline int rbw_for(int P) {
+  int rb = (P + 15) / 16;
+  int per = (rb + kWaves - 1) / kWaves;
+  int r = 1;
+  while (r < per) r <<= 1;
+  return r;
+}
+
+// Launchers (one per kernel family); return hipError_t.
+hipError_t launch_decode(const Args &a, hipStream_t s);
+hipError_t launch_verify(const Args &a, hipStream_t s);
+hipError_t launch_flush(const Args &a, hipStream_t s);
+hipError_t launch_conventional(const Args &a, hipStream_t s);
+hipError_t launch_init(const Args &a, hipStream_t s);
+hipError_t launch_commit(const Args &a, hipStream_t s);
+hipError_t launch_clear_err(int32_t *err, hipStream_t s);
+hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+// Kind-specific launchers (defined in kernels_m2.hip / kernels_gdn.hip).
+hipError_t launch_decode_m2(const Args &a, hipStream_t s);
+hipError_t launch_verify_m2(const Args &a, hipStream_t s);
+hipError_t launch_flush_m2(const Args &a, hipStream_t s);
+hipError_t launch_conventional_m2(const Args &a, hipStream_t s);
+hipError_t launch_decode_gdn(const Args &a, hipStream_t s);
+hipError_t launch_verify_gdn(const Args &a, hipStream_t s);
+hipError_t launch_flush_gdn(const Args &a, hipStream_t s);
+hipError_t launch_conventional_gdn(const Args &a, hipStream_t s);
+
+}  // namespace rssm

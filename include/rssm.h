@@ -1,0 +1,231 @@
+/*
+ * rssm.h -- C ABI of the ReplaySSM decode hot path for AMD MI355X (gfx950).
+ *
+ * The method (pages on ReplaySSM, "Cache SSM Inputs, Not State"): each sequence's
+ * recurrent state is held as an FP32 checkpoint S_ckpt plus a ring buffer of the
+ * input records appended since the checkpoint, with a cursor.  Non-flush decode
+ * steps append the record and compute only the output from checkpoint + ring;
+ * a flush folds the ring into the checkpoint and writes it once; speculative
+ * drafts are appended past the cursor, verified output-only, and the accepted
+ * prefix is committed by advancing the cursor.  Source passages:
+ *   - page 4 "ReplaySSM caches SSM inputs instead of state ...", section "What
+ *     shipped": the Mamba-2 update, the window of 16 records, flush, pointer
+ *     commit of drafts, and the output-only chunkwise verify form;
+ *   - page 1 (Japanese news article), sections on what the method does and on
+ *     what got faster: write once per window, rollback as a pointer move, and
+ *     the low-precision read copy that never re-enters the recurrence.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates and
+ *     owns every buffer; the library never allocates in these calls and keeps no
+ *     global mutable state.  Calls on distinct states and streams may run
+ *     concurrently; calls on one state must be ordered by the caller (one stream).
+ *   - Every call only ENQUEUES work on `stream` (NULL = the null stream) and
+ *     returns immediately, except rssm_get_error (synchronises).
+ *   - Host-side validation failure returns a negative RSSM_E_* code and enqueues
+ *     nothing.  batch == 0 is valid and enqueues nothing.
+ *   - Device-side contract violations set bits in the sticky error word
+ *     state->err and leave the offending sequence untouched (read it with
+ *     rssm_get_error).
+ *   - Inputs are fp32 or bf16 (raw bfloat16 bits, uint16_t) per config.in_dtype;
+ *     outputs are always fp32.  S_ckpt is fp32 [B][H][dv][dk], dk contiguous.
+ *   - Value head h uses key/query head h / (H / G) (contiguous groups).
+ *   - Alignment: s_ckpt, s_read and the conventional state must be 16-byte
+ *     aligned; every other pointer must be aligned to its element size.
+ */
+#ifndef RSSM_H
+#define RSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes (host side) */
+enum {
+  RSSM_OK = 0,
+  RSSM_E_NULL = -1,    /* a required pointer is NULL */
+  RSSM_E_SHAPE = -2,   /* unsupported or inconsistent sizes */
+  RSSM_E_DTYPE = -3,   /* unknown kind / in_dtype / read_copy */
+  RSSM_E_ALIGN = -4,   /* misaligned pointer */
+  RSSM_E_RANGE = -5,   /* argument out of range (T, min_records) */
+  RSSM_E_HIP = -6,     /* a HIP runtime call failed */
+  RSSM_E_DEVICE = -7   /* no usable gfx950 device */
+};
+
+/* bits of the device-side sticky error word */
+enum {
+  RSSM_DEVERR_VERIFY_CAPACITY = 1, /* verify: h + T > capacity; sequence untouched */
+  RSSM_DEVERR_ACCEPT_RANGE = 2,    /* commit: n_accept outside 0..T, or the verify it
+                                      commits could not append (h + T > capacity) */
+  RSSM_DEVERR_CURSOR = 4           /* counters inconsistent (h < 0 or h > capacity) */
+};
+
+enum { RSSM_KIND_MAMBA2 = 0, RSSM_KIND_GDN = 1 };
+enum { RSSM_DTYPE_F32 = 0, RSSM_DTYPE_BF16 = 1 };
+enum { RSSM_READ_NONE = 0, RSSM_READ_FP8 = 1, RSSM_READ_MXFP4 = 2 };
+
+/* (host) problem description.
+ *   kind       RSSM_KIND_MAMBA2: S <- a S + v k^T, y = S q (page 4, "What shipped").
+ *              RSSM_KIND_GDN: gated delta rule S <- a S (I - b k k^T) + b v k^T,
+ *              o = S q (the pages name it without a formula; published form).
+ *   batch      B >= 0 sequences.
+ *   n_heads    H value heads; n_qk_heads G key/query heads, H % G == 0.
+ *   dv, dk     P rows and N columns of a state tile.  dk in {32, 64, 128, 256};
+ *              1 <= dv <= 16384 / dk.
+ *   L          flush threshold (window length; the pages use 16), L >= 1.
+ *   t_max      maximum drafts per verify (1 = decode only), 1 <= t_max <= 8.
+ *   capacity   ring slots C, L + t_max - 1 <= C <= 32.
+ *   in_dtype   RSSM_DTYPE_F32 or RSSM_DTYPE_BF16 for alpha, beta, v, k, q and the ring.
+ *   read_copy  RSSM_READ_NONE, RSSM_READ_FP8 (OCP E4M3FN codes + one fp32 scale
+ *              amax/448 per 32 elements along dk) or RSSM_READ_MXFP4 (OCP MX
+ *              E2M1 codes, two per byte with the even element in the low nibble,
+ *              + one E8M0 scale 2^(floor(log2 amax) - 2) per 32 elements).  The copy
+ *              is written at init and at every flush, read by non-flush decode
+ *              steps only, and never feeds the recurrence (page 1, low-precision
+ *              section; page 4, quantisation paragraph). */
+typedef struct {
+  int32_t kind;
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_qk_heads;
+  int32_t dv;
+  int32_t dk;
+  int32_t L;
+  int32_t t_max;
+  int32_t capacity;
+  int32_t in_dtype;
+  int32_t read_copy;
+} rssm_config;
+
+/* (host) struct of caller-owned device buffers, sized by rssm_sizes.
+ *   s_ckpt        fp32 [B][H][dv][dk] checkpoint (the state as of the last flush).
+ *   s_read        read-copy codes: fp8 [B][H][dv][dk] bytes, or MXFP4 [B][H][dv][dk/2]
+ *                 bytes; NULL when read_copy == RSSM_READ_NONE.
+ *   s_read_scale  fp8: fp32 [B][H][dv][dk/32]; MXFP4: E8M0 bytes [B][H][dv][dk/32];
+ *                 NULL when read_copy == RSSM_READ_NONE.
+ *   ring          one buffer holding, at 256-byte aligned offsets in this order
+ *                 (element = in_dtype):
+ *                   alpha [B][H][C], beta [B][H][C] (GDN only, else absent),
+ *                   v [B][H][C][dv], k [B][G][C][dk], q [B][G][C][dk].
+ *                 Record of cursor position pos lives in slot pos % C.  Stored
+ *                 bits are exact copies of the appended inputs.
+ *   n_committed   int64 [B][H]: records committed since init (per-tile replicas of
+ *                 the per-sequence cursor; all H replicas of a sequence are equal).
+ *   n_ckpt        int64 [B][H]: cursor position of the checkpoint.  The ring holds
+ *                 h = n_committed - n_ckpt live records.
+ *   err           int32 [1] sticky device error word (RSSM_DEVERR_* bits). */
+typedef struct {
+  float *s_ckpt;
+  void *s_read;
+  void *s_read_scale;
+  void *ring;
+  int64_t *n_committed;
+  int64_t *n_ckpt;
+  int32_t *err;
+} rssm_state;
+
+/* (host) byte sizes of the buffers of rssm_state. */
+typedef struct {
+  size_t s_ckpt;
+  size_t s_read;
+  size_t s_read_scale;
+  size_t ring;
+  size_t n_committed;
+  size_t n_ckpt;
+  size_t err;
+} rssm_buffer_sizes;
+
+/* Host only.  Validate a config: RSSM_OK or a negative code. */
+int rssm_check_config(const rssm_config *cfg);
+
+/* Host only.  Fill `out` (host) with the byte size of every state buffer. */
+int rssm_sizes(const rssm_config *cfg, rssm_buffer_sizes *out);
+
+/* Host only.  Byte offsets of alpha, beta, v, k, q inside `ring` (out: host int64[5];
+ * beta's offset equals v's when kind is Mamba-2). */
+int rssm_ring_offsets(const rssm_config *cfg, int64_t *out5);
+
+/* Initialise a state: S_ckpt <- s0 (fp32 [B][H][dv][dk]) or zeros when s0 == NULL,
+ * write the read copy, zero the counters and the error word.  The ring content is
+ * left as is (no live records). */
+int rssm_init_state(const rssm_config *cfg, const rssm_state *st, const float *s0,
+                    hipStream_t stream);
+
+/* One decode step for every sequence (page 4 "What shipped"; page 1, what the
+ * method does).  Inputs: alpha [B][H], beta [B][H] (GDN; NULL for Mamba-2),
+ * v [B][H][dv], k [B][G][dk], q [B][G][dk].  Output y [B][H][dv] fp32.
+ * Per sequence with h = n_committed - n_ckpt live records before the step:
+ *   - if h + 1 < L: append the record at slot n_committed % C and write
+ *     y = G S_read q + sum_j decay(j -> now) (k_j . q) v_j (Mamba-2; GDN uses the
+ *     equivalent query-transform form) where S_read is S_ckpt or its read copy;
+ *     S_ckpt is not written;
+ *   - else (flush step): fold the h ring records and the current one into
+ *     S_ckpt, write it (and the read copy) once, set n_ckpt = n_committed + 1;
+ *     y = S_new q from the fp32 state.  The current record is not written to the
+ *     ring.
+ * Then n_committed += 1. */
+int rssm_decode_step(const rssm_config *cfg, const rssm_state *st, const void *alpha,
+                     const void *beta, const void *v, const void *k, const void *q,
+                     float *y, hipStream_t stream);
+
+/* Fold every sequence holding h >= max(min_records, 1) live records into S_ckpt
+ * (write once, plus the read copy) and set n_ckpt = n_committed; other sequences
+ * are untouched (page 4 "What shipped", flush).  min_records >= 0.  The
+ * speculative protocol calls rssm_flush(L) after every rssm_commit. */
+int rssm_flush(const rssm_config *cfg, const rssm_state *st, int32_t min_records,
+               hipStream_t stream);
+
+/* Speculative verify (page 4 "What shipped", verify paragraph): append T drafts
+ * (1 <= T <= t_max) at slots (n_committed + tau) % C without moving the cursor,
+ * and write the output-only chunk O [B][T][H][dv] fp32:
+ *   Mamba-2: O[:, tau] = G_{h+tau} S_ckpt q_tau + sum_{j <= h+tau} W[j, tau] (k_j . q_tau) v_j
+ *   GDN:     the same with pseudo-values from the delta rule's triangular system,
+ *            evaluated per draft in query-transform form.
+ * Draft inputs: alpha [B][T][H], beta [B][T][H] (GDN), v [B][T][H][dv],
+ * k [B][T][G][dk], q [B][T][G][dk].  S_ckpt is never written.  A sequence with
+ * h + T > C sets RSSM_DEVERR_VERIFY_CAPACITY and is left untouched (no ring
+ * write, its O rows not written). */
+int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const void *alpha,
+                const void *beta, const void *v, const void *k, const void *q, float *o,
+                hipStream_t stream);
+
+/* Commit the accepted prefix (page 4 "What shipped"; page 1, rollback as a pointer
+ * move): n_committed += n_accept[b] for every sequence, nothing else.  n_accept is
+ * int32 [B] on the device, each in 0..T where T is the preceding verify's T.  An
+ * out-of-range value (or a sequence whose verify could not append) sets
+ * RSSM_DEVERR_ACCEPT_RANGE and leaves that sequence untouched. */
+int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_accept,
+                int32_t T, hipStream_t stream);
+
+/* Conventional read-modify-write decode step, the comparison point (page 4 "What
+ * shipped": every token loads the full state, updates it and stores it back).
+ * s: fp32 [B][H][dv][dk] state, updated in place; inputs and y as in
+ * rssm_decode_step.  No ring, no cursor. */
+int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *alpha,
+                                  const void *beta, const void *v, const void *k,
+                                  const void *q, float *y, hipStream_t stream);
+
+/* Synchronise `stream`, return the device error word (>= 0, RSSM_DEVERR_* bits)
+ * and clear it; a negative code if a HIP call fails. */
+int rssm_get_error(const rssm_state *st, hipStream_t stream);
+
+/* Plain device-to-device copy of `bytes` bytes (16-byte aligned pointers, bytes a
+ * multiple of 16) with a streaming kernel; used to calibrate bandwidth and
+ * profiler byte counters against a kernel of known traffic. */
+int rssm_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+/* Static description of a return code or device error bit set. */
+const char *rssm_strerror(int code);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int rssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSSM_H */

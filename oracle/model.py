@@ -19,8 +19,9 @@ plain definition of what every output must equal) plus the integer cursor:
 * verify(T): draft tau goes to slot ``(n_committed + tau) % C``; the counters do
   not move; output tau is the stepwise recurrence over drafts 0..tau applied to
   a temporary copy of S, which is then discarded.  Requires ``h + T <= C``.
-* commit(a): ``0 <= a <= T`` and ``h + a <= C``; the first ``a`` drafts advance S
-  stepwise; ``n_committed += a``.  Nothing else.
+* commit(a): ``0 <= a <= T`` and ``h + T <= C`` (the verify being committed could
+  append its drafts); the first ``a`` drafts advance S stepwise;
+  ``n_committed += a``.  Nothing else.
 * flush(min_records): sequences with ``h >= max(min_records, 1)`` make the
   checkpoint equal S and set ``n_ckpt = n_committed``.
 * read copy (decode only): at init and at every flush the float32 checkpoint
@@ -110,6 +111,8 @@ class ReplayOracle:
         return out
 
     def _store(self, i: int, slot: int, inp, t: Optional[int] = None):
+        if not self.track_state:
+            return
         for f in _FIELDS:
             a = inp.get(f)
             if a is None:
@@ -176,7 +179,7 @@ class ReplayOracle:
         for i in range(len(self.seqs)):
             a = int(accept[i])
             h = self.n_committed[i] - self.n_ckpt[i]
-            if a < 0 or a > T or h + a > wl.capacity or not self._draft_ok[i]:
+            if a < 0 or a > T or h + T > wl.capacity or not self._draft_ok[i]:
                 self.err = True
                 continue
             if self.track_state:

@@ -14,9 +14,10 @@ their hardware.  The two formats here are the published OCP ones:
 * MXFP4 (OCP Microscaling v1.0): E2M1 elements (1 sign, 2 exponent bits with
   bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one E8M0
   scale 2^E per 32 elements, E = floor(log2(amax)) - 2 (2 = largest E2M1
-  exponent), clamped to [-127, 127]; element code = E2M1 round-to-nearest-even
-  of x / 2^E, saturating to +-6.  amax == 0 gives E = -127.  Two codes per byte,
-  even element in the low nibble.
+  exponent), clamped to [-126, 127] so that the scale is a normal float32
+  (reading: E8M0 can also encode 2^-127, which is not used); element code =
+  E2M1 round-to-nearest-even of x / 2^E, saturating to +-6.  amax == 0 gives
+  E = -126.  Two codes per byte, even element in the low nibble.
 
 The rounding here is done on exact float64 values (quantum = 2^(e - mbits)),
 not with bit tricks, so it is an independent statement of the format rules.
@@ -132,8 +133,8 @@ def quantize_mxfp4_blocks(x32: np.ndarray):
     amax = np.max(np.abs(xb), axis=-1)
     with np.errstate(divide="ignore"):
         _, ex = np.frexp(amax)
-    E = np.where(amax > 0, (ex - 1) - 2, -127)
-    E = np.clip(E, -127, 127)
+    E = np.where(amax > 0, (ex - 1) - 2, -126)
+    E = np.clip(E, -126, 127)
     y = xb / np.ldexp(1.0, E)[..., None]                              # exact
     codes = e2m1_encode(y).reshape(x32.shape)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)

@@ -1,0 +1,129 @@
+"""GPU parity of the low-precision read copy (fp8 E4M3 / MXFP4): quantiser bits,
+exact readout through the non-flush path, outputs against the oracle, and the
+invariant that the fp32 checkpoint trajectory is untouched by the copy."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import (ReplayOracle, dequantize_fp8_blocks, dequantize_mxfp4_blocks,
+                    quantize_fp8_blocks, quantize_mxfp4_blocks)
+from synth import decode_inputs, get_workload, initial_state
+from synth.stream import StepSource
+
+from gpu_util import (TOL_READ, decode, dev, new_state, relerr, to_dev_inputs)
+from oracle_runs import decode_runs
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(fmt, **kw):
+    base = dict(name="rc", batch=3, n_heads=4, n_qk_heads=4, dv=40, dk=64, in_dtype="fp32", L=5,
+                capacity=5, read_copy=fmt)
+    base.update(kw)
+    return get_workload("m2_readcopy_b256").replace(**base)
+
+
+def _special_s0(wl):
+    S0 = initial_state(wl, range(wl.batch))
+    S0[0, 0, 0, :32] = 0.0                       # all-zero block
+    S0[0, 0, 1, :32] = 2.0 ** -140               # tiny block (denormal values)
+    S0[0, 1, 2, :] = np.float32(448.0)           # exact maximum
+    S0[1, 0, 3, 5] = 1e4                          # one large outlier per block
+    return S0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_init_quantiser_bits(fmt, dk):
+    wl = _wl(fmt, dk=dk)
+    S0 = _special_s0(wl)
+    ds = new_state(wl, S0)
+    codes, scales = ds.read_copy()
+    if fmt == "fp8":
+        rc, rs = quantize_fp8_blocks(S0)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    else:
+        rc, rs = quantize_mxfp4_blocks(S0)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+        assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_exact_readout_through_decode(fmt):
+    """alpha = 1, v = 0, k = 0, q = e_n: a non-flush output is column n of the dequantised
+    copy (one rounding of code * scale), a flush output is column n of the fp32 state."""
+    wl = _wl(fmt, dk=32, L=5, capacity=5)
+    B, H, P, N = wl.batch, wl.n_heads, wl.dv, wl.dk
+    S0 = _special_s0(wl)
+    ds = new_state(wl, S0)
+    if fmt == "fp8":
+        deq = dequantize_fp8_blocks(*quantize_fp8_blocks(S0))
+    else:
+        deq = dequantize_mxfp4_blocks(*quantize_mxfp4_blocks(S0))
+    deq32 = deq.astype(np.float32)
+    y = torch.empty(B, H, P, device="cuda")
+    inp = {"alpha": np.ones((B, H), np.float32), "beta": None, "v": np.zeros((B, H, P), np.float32),
+           "k": np.zeros((B, H, N), np.float32)}
+    for t in range(5 * N):
+        n = t % N
+        q = np.zeros((B, H, N), np.float32)
+        q[:, :, n] = 1.0
+        decode(ds, to_dev_inputs(dict(inp, q=q)), y)
+        got = y.cpu().numpy()
+        flush = (t + 1) % wl.L == 0
+        want = S0[:, :, :, n] if flush else deq32[:, :, :, n]
+        # exact equality (a code for -0 reads back as +0 through the FMA chain, so compare values)
+        assert np.array_equal(got, want), f"step {t} column {n} flush={flush}"
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(40, 64, "fp32"), (17, 32, "bf16"), (128, 128, "bf16")])
+def test_decode_with_read_copy_matches_oracle(fmt, shape):
+    P, N, dt = shape
+    wl = _wl(fmt, dv=P, dk=N, in_dtype=dt, L=6, capacity=6)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    plain = new_state(wl.replace(read_copy="none"), S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    for t in range(20):
+        inp = decode_inputs(wl, t, seqs)
+        d = to_dev_inputs(inp)
+        decode(ds, d, y)
+        decode(plain, d, y2)
+        yr = orc.decode(inp)
+        err = relerr(y.cpu().numpy(), yr).max()
+        assert err <= TOL_READ, f"step {t}: rel err {err:.3g}"
+        # the copy never feeds the recurrence: checkpoints are bit-identical to the plain run
+        assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32))
+        if (t + 1) % wl.L == 0:
+            assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert ds.error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_serving_shape_read_copy_sampled(fmt):
+    """Mamba-2 serving shape (B=256, H=128, P=64, N=128, bf16) with a read copy, 512 steps."""
+    wl = get_workload("m2_readcopy_b256").replace(read_copy=fmt)
+    steps = 512
+    seqs = list(range(wl.batch))
+    sample = [0, 100, 255]
+    print(f"[read copy {fmt}] oracle runs for {sample}", flush=True)
+    ref = decode_runs(wl, sample, steps)
+    ds = new_state(wl, initial_state(wl, seqs))
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    idx = torch.tensor(sample, device="cuda")
+    worst = 0.0
+    with StepSource(wl, seqs) as src:
+        for t in range(steps):
+            decode(ds, to_dev_inputs(src.decode(t)), y)
+            got = y[idx].cpu().numpy()
+            for i, b in enumerate(sample):
+                worst = max(worst, relerr(got[i], ref[b]["y"][t]).max())
+            if t % 128 == 127:
+                print(f"[read copy {fmt}] step {t + 1}/{steps} worst rel err {worst:.3g}", flush=True)
+    assert worst <= TOL_READ
+    assert ds.error() == 0

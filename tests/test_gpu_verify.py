@@ -1,0 +1,240 @@
+"""GPU parity of the speculative path (verify -> commit -> flush) for Mamba-2 and
+Gated DeltaNet, rollback invariants and device-side contract errors."""
+import numpy as np
+import pytest
+import torch
+
+from attention_decode_mamba_amd import rssm as R
+from oracle import ReplayOracle
+from synth import accept_counts, decode_inputs, draft_inputs, get_workload, initial_state
+from synth.stream import StepSource
+
+from gpu_util import (TOL, assert_counters, counters, decode, dev, new_state, ptr, relerr, ring_bits,
+                      stream, tile_relerr, to_dev_inputs, verify)
+from oracle_runs import cursor_run, spec_runs
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(name, **kw):
+    wl = get_workload(name)
+    if name.startswith("gdn"):
+        base = dict(batch=6, n_heads=4, n_qk_heads=2, dv=48, dk=64)
+    else:
+        base = dict(batch=6, n_heads=4, n_qk_heads=4, dv=20, dk=32)
+    base.update(kw)
+    return wl.replace(name="small", **base)
+
+
+def _commit(ds, acc, T):
+    R.rssm_commit(ds.cfg, ds.st, ptr(acc), T, stream())
+
+
+def _flush(ds, m):
+    R.rssm_flush(ds.cfg, ds.st, m, stream())
+
+
+def _poison_rejected(ds, nc_before, acc, T):
+    """Overwrite the ring slots of rejected drafts with NaN bit patterns (host-side writes)."""
+    ring = ds.ring_arrays()
+    C = ds.cfg.capacity
+    nan = -1 if ring["v"].dtype == torch.int16 else float("nan")     # 0xFFFF is a bf16 NaN
+    for b in range(ds.cfg.batch):
+        for tau in range(int(acc[b]), T):
+            slot = int((nc_before[b] + tau) % C)
+            ring["alpha"][b, :, slot] = nan
+            ring["v"][b, :, slot] = nan
+            ring["k"][b, :, slot] = nan
+            ring["q"][b, :, slot] = nan
+            if ring["beta"] is not None:
+                ring["beta"][b, :, slot] = nan
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_spec_small(name, dtype):
+    """A few decode steps, then verify(T) / commit(a) / flush(L): outputs, cursors, checkpoints."""
+    wl = _small(name, in_dtype=dtype)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    for t in range(5):
+        inp = decode_inputs(wl, t, seqs)
+        decode(ds, to_dev_inputs(inp), y)
+        assert relerr(y.cpu().numpy(), orc.decode(inp)).max() <= TOL
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(40):
+        d = draft_inputs(wl, s, seqs, T)
+        verify(ds, T, to_dev_inputs(d), o)
+        Or = orc.verify(d, T)
+        err = relerr(o.cpu().numpy(), Or).max()
+        assert err <= TOL, f"verify step {s}: rel err {err:.3g}"
+        acc = accept_counts(wl, s, T)[: wl.batch]
+        _commit(ds, dev(acc), T)
+        orc.commit(acc, T)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"commit {s}")
+        _flush(ds, wl.L)
+        orc.flush(wl.L)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"flush {s}")
+        e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
+        assert e <= TOL, f"step {s}: checkpoint rel err {e:.3g}"
+    # a decode step after speculation continues from the same cursor
+    inp = decode_inputs(wl, 99, seqs)
+    decode(ds, to_dev_inputs(inp), y)
+    assert relerr(y.cpu().numpy(), orc.decode(inp)).max() <= TOL
+    assert_counters(ds, orc.n_committed, orc.n_ckpt, "final decode")
+    assert ds.error() == 0
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+def test_rejected_slots_are_never_read(name):
+    """Poisoning every rejected draft slot with NaN changes no output and no checkpoint bit."""
+    wl = _small(name)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    A, B = new_state(wl, S0), new_state(wl, S0)
+    oa = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    ob = torch.empty_like(oa)
+    for s in range(30):
+        d = to_dev_inputs(draft_inputs(wl, s, seqs, T))
+        verify(A, T, d, oa)
+        verify(B, T, d, ob)
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), f"step {s}"
+        acc = accept_counts(wl, s, T)[: wl.batch]
+        nc_before = counters(B)[0][:, 0].copy()
+        _commit(A, dev(acc), T)
+        _commit(B, dev(acc), T)
+        torch.cuda.synchronize()
+        _poison_rejected(B, nc_before, acc, T)
+        _flush(A, wl.L)
+        _flush(B, wl.L)
+        assert torch.equal(A.ckpt().view(torch.int32), B.ckpt().view(torch.int32)), f"step {s}"
+    assert A.error() == 0 and B.error() == 0
+
+
+def test_device_errors_leave_sequences_untouched():
+    wl = _small("m2_verify_b512")
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    ds = new_state(wl, initial_state(wl, seqs))
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    acc = np.zeros(wl.batch, np.int32)
+    acc[0] = T                                   # sequence 0 commits T per step, never flushed
+    for s in range(4):
+        verify(ds, T, to_dev_inputs(draft_inputs(wl, s, seqs, T)), o)
+        _commit(ds, dev(acc), T)
+    assert ds.error() == 0
+    nc, nk = counters(ds)
+    assert np.all(nc[0] == 4 * T) and np.all(nc[1:] == 0)
+    ring0 = {k: (None if v is None else v[0].clone()) for k, v in ds.ring_arrays().items()}
+    ck_before = ds.ckpt().clone()
+    o.fill_(7.0)
+    verify(ds, T, to_dev_inputs(draft_inputs(wl, 9, seqs, T)), o)
+    err = ds.error()
+    assert err & R.RSSM_DEVERR_VERIFY_CAPACITY
+    assert torch.all(o[0] == 7.0)                # rows of the refused sequence not written
+    assert torch.all(o[1:] != 7.0)
+    after = ds.ring_arrays()
+    for k, v in ring0.items():                   # the refused sequence's ring rows are unchanged
+        if v is not None:
+            assert torch.equal(v, after[k][0]), k
+    assert torch.equal(ck_before, ds.ckpt())
+    # commit of the refused verify is refused too
+    acc2 = np.ones(wl.batch, np.int32)
+    _commit(ds, dev(acc2), T)
+    assert ds.error() & R.RSSM_DEVERR_ACCEPT_RANGE
+    nc2, _ = counters(ds)
+    assert np.all(nc2[0] == 4 * T) and np.all(nc2[1:] == 1)
+    # out-of-range accepted count
+    acc3 = np.zeros(wl.batch, np.int32)
+    acc3[1] = T + 1
+    verify(ds, T, to_dev_inputs(draft_inputs(wl, 10, seqs, T)), o)
+    _commit(ds, dev(acc3), T)
+    e = ds.error()
+    assert e & R.RSSM_DEVERR_ACCEPT_RANGE
+    nc3, _ = counters(ds)
+    assert np.all(nc3[1] == 1) and np.all(nc3[2:] == 1)
+    # flushing repairs sequence 0 and the protocol continues
+    _flush(ds, wl.L)
+    assert ds.error() == 0
+    _, nk4 = counters(ds)
+    assert np.all(nk4[0] == 4 * T)
+
+
+SAMPLE4 = [0, 171, 342, 511]
+
+
+def test_serving_shape_verify_sampled():
+    """Mamba-2 verify at B=512, H=128, P=64, N=128, T=4, 128 steps; accepted prefix ~ U{0..4}."""
+    wl = get_workload("m2_verify_b512")
+    T, steps = wl.t_max, wl.verify_steps
+    seqs = list(range(wl.batch))
+    print(f"[serving verify] oracle runs for {SAMPLE4}", flush=True)
+    ref = spec_runs(wl, SAMPLE4, 0, steps, T, ckpt_every=32)
+    cur = cursor_run(wl, steps, verify=True, T=T)
+    ds = new_state(wl, initial_state(wl, seqs))
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    idx = torch.tensor(SAMPLE4, device="cuda")
+    worst = 0.0
+    with StepSource(wl, seqs) as src:
+        for s in range(steps):
+            verify(ds, T, to_dev_inputs(src.drafts(s, T)), o)
+            got = o[idx].cpu().numpy()
+            for i, b in enumerate(SAMPLE4):
+                worst = max(worst, relerr(got[i], ref[b]["O"][s]).max())
+            _commit(ds, dev(accept_counts(wl, s, T)), T)
+            _flush(ds, wl.L)
+            assert_counters(ds, *cur[s], f"step {s}")
+            for b in SAMPLE4:
+                if s in ref[b]["ckpt"]:
+                    e = tile_relerr(ds.ckpt()[b].cpu().numpy(), ref[b]["ckpt"][s]).max()
+                    assert e <= TOL, f"step {s} seq {b}: checkpoint rel err {e:.3g}"
+            if s % 32 == 31:
+                print(f"[serving verify] step {s + 1}/{steps} worst rel err {worst:.3g}", flush=True)
+    assert worst <= TOL
+    assert ds.error() == 0
+
+
+def test_serving_shape_gdn_decode_then_verify_sampled():
+    """Gated DeltaNet at B=256, 32 value / 16 key heads, 128 x 128 tiles: 256 decode steps,
+    then 256 verify steps with T = 4 drafts."""
+    wl = get_workload("gdn_b256")
+    T = wl.t_max
+    nd, nv = wl.decode_steps, wl.verify_steps
+    seqs = list(range(wl.batch))
+    sample = [0, 128, 255]
+    print(f"[serving gdn] oracle runs for {sample}", flush=True)
+    ref = spec_runs(wl, sample, nd, nv, T, ckpt_every=64)
+    cur = cursor_run(wl, nv, verify=True, T=T, decode_steps=nd)
+    ds = new_state(wl, initial_state(wl, seqs))
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    idx = torch.tensor(sample, device="cuda")
+    worst_d = worst_v = 0.0
+    with StepSource(wl, seqs) as src:
+        for t in range(nd):
+            decode(ds, to_dev_inputs(src.decode(t)), y)
+            got = y[idx].cpu().numpy()
+            for i, b in enumerate(sample):
+                worst_d = max(worst_d, relerr(got[i], ref[b]["y"][t]).max())
+        print(f"[serving gdn] decode worst rel err {worst_d:.3g}", flush=True)
+        for s in range(nv):
+            verify(ds, T, to_dev_inputs(src.drafts(s, T)), o)
+            got = o[idx].cpu().numpy()
+            for i, b in enumerate(sample):
+                worst_v = max(worst_v, relerr(got[i], ref[b]["O"][s]).max())
+            _commit(ds, dev(accept_counts(wl, s, T)), T)
+            _flush(ds, wl.L)
+            assert_counters(ds, *cur[s], f"verify step {s}")
+            for b in sample:
+                if s in ref[b]["ckpt"]:
+                    e = tile_relerr(ds.ckpt()[b].cpu().numpy(), ref[b]["ckpt"][s]).max()
+                    assert e <= TOL, f"step {s} seq {b}: checkpoint rel err {e:.3g}"
+            if s % 64 == 63:
+                print(f"[serving gdn] verify step {s + 1}/{nv} worst rel err {worst_v:.3g}", flush=True)
+    assert worst_d <= TOL and worst_v <= TOL
+    assert ds.error() == 0

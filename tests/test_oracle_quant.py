@@ -90,14 +90,16 @@ def test_mxfp4_shared_scale_definition():
     x[4, :] = 0.0
     x[4, 7] = 4.0          # power-of-two amax
     x[5, 0] = -1e-40       # denormal amax candidate is dominated by others in that row
+    x[6, :] = 0.0
+    x[6, 3] = 2.0 ** -130  # tiny block: exponent clamps to -126
     packed, e8 = quantize_mxfp4_blocks(x)
     for r in range(64):
         amax = float(np.max(np.abs(x[r].astype(np.float64))))
         if amax == 0:
-            assert e8[r, 0] == 0
+            assert e8[r, 0] == 1          # 2^-126, the smallest scale used
             continue
         E = math.floor(math.log2(amax)) - g["e2m1_emax"]
-        assert int(e8[r, 0]) == max(min(E, 127), -127) + g["e8m0_bias"]
+        assert int(e8[r, 0]) == max(min(E, 127), -126) + g["e8m0_bias"]
     deq = dequantize_mxfp4_blocks(packed, e8)
     assert deq.shape == x.shape
     # every element within half a step of its binade (or clipped to 6 * 2^E)
