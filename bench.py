@@ -26,7 +26,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 METRIC = "SSM decode tokens/s + effective HBM GB/s (% of peak), B=256 H128 P64 N128 fp32"
 WORKLOAD = "m2_decode_b256"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_mamba2_b256_h128_p64_n128_counters.json")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_mamba2_b256_h128_p64_n128_counters.txt")
+COPY_BYTES = 1 << 30            # size of each calibration copy (read and written)
 KERNEL_SOURCES = ["attention_decode_mamba_amd/csrc/rssm_device.hpp",
                   "attention_decode_mamba_amd/csrc/kernels_m2.hip"]
 
@@ -204,7 +205,7 @@ def run(args) -> dict:
     cb = conventional_bytes(wl)
 
     # achievable bandwidth of a plain streaming copy (context for the roofline fraction)
-    nbytes = 1 << 30
+    nbytes = COPY_BYTES
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     R.rssm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
@@ -261,6 +262,66 @@ def run(args) -> dict:
     return res
 
 
+def _read_counter_csv(path):
+    """rocprofv3 counter_collection CSV -> {dispatch_id: (kernel_name, {counter: value})}."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            did = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            name = row.get("Kernel_Name", "")
+            cn = row.get("Counter_Name")
+            val = float(row.get("Counter_Value") or 0.0)
+            ent = out.setdefault(did, (name, {}))
+            ent[1][cn] = ent[1].get(cn, 0.0) + val
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps):
+    """Per-launch HBM traffic of the decode and conventional kernels from two --pmc runs
+    (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
+    reads for the streaming copy of COPY_BYTES bytes."""
+    from synth import get_workload
+    wl = get_workload(WORKLOAD).replace(batch=batch)
+    res = {"kernel_source_hash": kernel_source_hash(), "batch": batch, "command": command}
+    fetch = _read_counter_csv(fetch_csv)
+    write = _read_counter_csv(write_csv)
+
+    def per_kernel(table, counter, key):
+        vals = [c.get(counter, 0.0) for n, c in table.values() if key in n]
+        return vals
+
+    cf = per_kernel(fetch, "FETCH_SIZE", "k_stream_copy")
+    cw = per_kernel(write, "WRITE_SIZE", "k_stream_copy")
+    known_kib = COPY_BYTES / 1024.0
+    ff = known_kib / (sum(cf) / len(cf))
+    fw = known_kib / (sum(cw) / len(cw))
+    res["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_mean": sum(cf) / len(cf),
+                               "write_kib_mean": sum(cw) / len(cw), "fetch_scale": ff, "write_scale": fw,
+                               "dispatches": len(cf)}
+    for key, label in (("k_decode", "replay_decode"), ("k_conventional", "conventional")):
+        f = per_kernel(fetch, "FETCH_SIZE", key)
+        w = per_kernel(write, "WRITE_SIZE", key)
+        if not f or not w:
+            continue
+        fb = sum(f) / len(f) * 1024.0 * ff
+        wb = sum(w) / len(w) * 1024.0 * fw
+        res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                      "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
+                      "write_kib_per_dispatch": w}
+    W = 16
+    hs = [((W + i) % wl.L) + 1 for i in range(steps)]
+    alg = sum(step_bytes(wl, h)["total"] for h in hs) / steps
+    res["algorithmic_bytes_per_launch"] = alg
+    if "replay_decode" in res:
+        r = res["replay_decode"]
+        res["traffic_bytes_per_launch"] = r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
+        res["traffic_over_algorithmic"] = res["traffic_bytes_per_launch"] / alg
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,7 +330,15 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch (default: 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the counter summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counter-command", default="", help="command recorded in the counter summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], PROFILE_SUMMARY,
+                               args.counter_command, args.batch or 256, args.steps)
+        print(json.dumps({k: v for k, v in r.items() if k != "replay_decode"}, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path shards over "
                                    "sequences/heads with no exchange, so N GPUs run N independent copies"}))

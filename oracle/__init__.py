@@ -31,7 +31,7 @@ from .quant import (
     e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
     quantize_fp8_blocks, dequantize_fp8_blocks,
     quantize_mxfp4_blocks, dequantize_mxfp4_blocks,
-    read_copy_dequant,
+    read_copy_dequant, read_copy_ambiguity,
 )
 from .model import ReplayOracle, OracleError
 from . import replay_forms
@@ -41,5 +41,6 @@ __all__ = [
     "e4m3_encode", "e4m3_decode", "e2m1_encode", "e2m1_decode",
     "quantize_fp8_blocks", "dequantize_fp8_blocks",
     "quantize_mxfp4_blocks", "dequantize_mxfp4_blocks", "read_copy_dequant",
+    "read_copy_ambiguity",
     "ReplayOracle", "OracleError", "replay_forms",
 ]

@@ -40,7 +40,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 from .recurrence import widen, step
-from .quant import read_copy_dequant
+from .quant import read_copy_dequant, read_copy_ambiguity
 
 
 class OracleError(ValueError):
@@ -59,7 +59,7 @@ class ReplayOracle:
     """
 
     def __init__(self, wl, seqs: Sequence[int], S0: Optional[np.ndarray] = None,
-                 track_state: bool = True):
+                 track_state: bool = True, read_tol: Optional[float] = None):
         if wl.n_heads % wl.n_qk_heads:
             raise OracleError("H % G != 0")
         if wl.capacity < wl.L + wl.t_max - 1:
@@ -92,8 +92,18 @@ class ReplayOracle:
             self.S = S0.astype(np.float64)
             self.S_ckpt = self.S.copy()
             self.R = None
+            # read-copy ambiguity (Mamba-2): A bounds |dS_read| elementwise for a checkpoint that
+            # agrees with S to read_tol (normwise per tile); G is the checkpoint decay since the
+            # last fold, so |dy| <= G * (A |q|) per output row.
+            self.read_tol = read_tol
+            self.allowance = np.zeros((nb, H, P))
             if wl.read_copy != "none":
                 self.R = read_copy_dequant(wl.read_copy, S0.astype(np.float32))
+                if read_tol is not None:
+                    if wl.kind != "mamba2":
+                        raise OracleError("read-copy ambiguity is modelled for Mamba-2 only")
+                    self.Ramb = np.stack([self._ambiguity(S0[i].astype(np.float64)) for i in range(nb)])
+                    self.Rgam = np.ones((nb, H))
 
     # -- helpers ---------------------------------------------------------------
     def h(self) -> np.ndarray:
@@ -119,10 +129,17 @@ class ReplayOracle:
                 continue
             self.ring[f][i, slot] = a[i] if t is None else a[i, t]
 
+    def _ambiguity(self, S):
+        delta = self.read_tol * np.max(np.abs(S), axis=(-2, -1), keepdims=True)
+        return read_copy_ambiguity(self.wl.read_copy, S.astype(np.float32), delta)
+
     def _checkpoint(self, i: int):
         self.S_ckpt[i] = self.S[i]
         if self.R is not None:
             self.R[i] = read_copy_dequant(self.wl.read_copy, self.S[i].astype(np.float32))
+            if self.read_tol is not None:
+                self.Ramb[i] = self._ambiguity(self.S[i])
+                self.Rgam[i] = 1.0
 
     # -- operations ------------------------------------------------------------
     def decode(self, inp) -> np.ndarray:
@@ -140,8 +157,14 @@ class ReplayOracle:
                 self.S[i], y_full = step(wl.kind, self.S[i], rec)
                 if self.R is not None and not flush:
                     self.R[i], y[i] = step(wl.kind, self.R[i], rec)
+                    if self.read_tol is not None:
+                        self.Rgam[i] = self.Rgam[i] * rec["alpha"]
+                        qh = np.repeat(np.abs(rec["q"]), wl.group, axis=0)
+                        self.allowance[i] = self.Rgam[i][:, None] * np.einsum("hpn,hn->hp", self.Ramb[i], qh)
                 else:
                     y[i] = y_full
+                    if self.R is not None and self.read_tol is not None:
+                        self.allowance[i] = 0.0
             if flush:
                 self.n_ckpt[i] = self.n_committed[i]
                 self.flush_count[i] += 1

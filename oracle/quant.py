@@ -109,10 +109,14 @@ def _blocks(x32: np.ndarray) -> np.ndarray:
     return x32.reshape(x32.shape[:-1] + (x32.shape[-1] // BLOCK, BLOCK))
 
 
-def quantize_fp8_blocks(x32: np.ndarray):
-    """float32 [..., N] -> (codes uint8 [..., N], scales float32 [..., N/32])."""
+def quantize_fp8_blocks(x32: np.ndarray, amax=None):
+    """float32 [..., N] -> (codes uint8 [..., N], scales float32 [..., N/32]).
+
+    ``amax`` (float32 [..., N/32]) overrides the block maxima (used to bound ambiguity)."""
     xb = _blocks(x32)
-    amax = np.max(np.abs(xb), axis=-1)                               # float32
+    if amax is None:
+        amax = np.max(np.abs(xb), axis=-1)                           # float32
+    amax = np.asarray(amax, np.float32)
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)         # float32 division
     safe = np.where(scale == 0, np.float32(1), scale).astype(np.float32)
     y = (xb / safe[..., None]).astype(np.float32)                    # float32 division
@@ -127,14 +131,21 @@ def dequantize_fp8_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return val.reshape(codes.shape)
 
 
-def quantize_mxfp4_blocks(x32: np.ndarray):
-    """float32 [..., N] -> (packed codes uint8 [..., N/2], E8M0 uint8 [..., N/32])."""
-    xb = _blocks(x32).astype(np.float64)
-    amax = np.max(np.abs(xb), axis=-1)
+def _mx_exponent(amax: np.ndarray) -> np.ndarray:
     with np.errstate(divide="ignore"):
         _, ex = np.frexp(amax)
     E = np.where(amax > 0, (ex - 1) - 2, -126)
-    E = np.clip(E, -126, 127)
+    return np.clip(E, -126, 127)
+
+
+def quantize_mxfp4_blocks(x32: np.ndarray, amax=None):
+    """float32 [..., N] -> (packed codes uint8 [..., N/2], E8M0 uint8 [..., N/32]).
+
+    ``amax`` overrides the block maxima (used to bound ambiguity)."""
+    xb = _blocks(x32).astype(np.float64)
+    if amax is None:
+        amax = np.max(np.abs(xb), axis=-1)
+    E = _mx_exponent(np.asarray(amax, np.float64))
     y = xb / np.ldexp(1.0, E)[..., None]                              # exact
     codes = e2m1_encode(y).reshape(x32.shape)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
@@ -157,3 +168,58 @@ def read_copy_dequant(fmt: str, x32: np.ndarray) -> np.ndarray:
     if fmt == "mxfp4":
         return dequantize_mxfp4_blocks(*quantize_mxfp4_blocks(x32))
     raise ValueError(fmt)
+
+
+def read_copy_ambiguity(fmt: str, x32: np.ndarray, delta) -> np.ndarray:
+    """Bound on |dequant(x') - dequant(x)| per element when every float32 input may differ
+    by at most ``delta`` (absolute, broadcast against x) from x.
+
+    Reading: the copy is made from the fp32 checkpoint the GPU holds, which agrees with the
+    oracle's only up to fp32 reassociation; an element (or, for MXFP4, a block maximum) that
+    lies that close to a rounding boundary has two correct codes.  Codes are monotone in x
+    for a fixed scale and in the scale for a fixed x, so the extreme codes come from the
+    corners x +- delta, amax +- delta, and the extreme dequantised values from the extreme
+    codes times the extreme scales.
+    """
+    x32 = np.asarray(x32, np.float32)
+    delta = np.broadcast_to(np.asarray(delta, np.float64), x32.shape)
+    xb = _blocks(x32).astype(np.float64)
+    db = delta.reshape(xb.shape)
+    amax = np.max(np.abs(xb), axis=-1)
+    damax = np.max(db, axis=-1)
+    base = read_copy_dequant(fmt, x32)
+    lo_c = hi_c = None
+    scales = []
+    for sa in (-1.0, 1.0):
+        am = np.maximum(amax + sa * damax, 0.0)
+        if fmt == "fp8":
+            am32 = am.astype(np.float32)
+            scales.append((am32 / np.float32(E4M3_MAX)).astype(np.float32).astype(np.float64))
+        else:
+            scales.append(np.ldexp(1.0, _mx_exponent(am)))
+        for sx in (-1.0, 1.0):
+            xp = (xb + sx * db).astype(np.float32).reshape(x32.shape)
+            if fmt == "fp8":
+                codes, _ = quantize_fp8_blocks(xp, amax=am.astype(np.float32))
+                val = e4m3_decode(codes.reshape(xb.shape))
+                val = np.where((am.astype(np.float32) / np.float32(E4M3_MAX) == 0)[..., None], 0.0, val)
+            else:
+                packed, _ = quantize_mxfp4_blocks(xp, amax=am)
+                lo = packed & 0xF
+                hi = packed >> 4
+                c = np.stack([lo, hi], axis=-1).reshape(x32.shape)
+                val = e2m1_decode(c.reshape(xb.shape))
+            lo_c = val if lo_c is None else np.minimum(lo_c, val)
+            hi_c = val if hi_c is None else np.maximum(hi_c, val)
+    s_lo = np.minimum(scales[0], scales[1])[..., None]
+    s_hi = np.maximum(scales[0], scales[1])[..., None]
+    b = base.reshape(xb.shape)
+    worst = np.zeros_like(b)
+    for c in (lo_c, hi_c):
+        for sc in (s_lo, s_hi):
+            worst = np.maximum(worst, np.abs(c * sc - b))
+    # a block whose maximum is within delta of zero has no determined scale: any dequantised
+    # value is within 1.5 (amax + delta) of zero (E2M1 saturation; E4M3 rounds by < 2^-4)
+    degenerate = (amax - damax) <= 0
+    worst = np.where(degenerate[..., None], 3.0 * (amax + damax)[..., None], worst)
+    return worst.reshape(x32.shape)

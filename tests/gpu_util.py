@@ -82,3 +82,13 @@ def ring_bits(arr):
     """A torch ring view -> numpy with the same bit patterns as the stored inputs."""
     a = arr.cpu().numpy()
     return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def read_copy_excess(got, ref, allowance):
+    """Per output row: |got - ref| minus (TOL * ||ref||_inf + the oracle's ambiguity allowance).
+    Positive values are violations.  Rows without an ambiguous element must match to fp32 level;
+    rows with one may differ by at most the bound on the dequantised change."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    return np.abs(got - ref) - (TOL * scale + np.asarray(allowance) * (1 + 1e-9))

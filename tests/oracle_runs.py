@@ -15,17 +15,24 @@ from synth import accept_counts, decode_inputs, draft_inputs, initial_state
 from synth.gen import default_workers
 
 
+READ_TOL = 2e-5   # the fp32-state tolerance the GPU checkpoint is held to
+
+
 def _decode_seq(args):
     wl, b, steps, keep_ckpt = args
-    orc = ReplayOracle(wl, [b], initial_state(wl, [b]))
-    ys, nc, nk, ck = [], [], [], {}
+    rt = READ_TOL if wl.read_copy != "none" else None
+    orc = ReplayOracle(wl, [b], initial_state(wl, [b]), read_tol=rt)
+    ys, nc, nk, ck, al = [], [], [], {}, []
     for t in range(steps):
         ys.append(orc.decode(decode_inputs(wl, t, [b]))[0])
+        if rt is not None:
+            al.append(orc.allowance[0].copy())
         nc.append(int(orc.n_committed[0]))
         nk.append(int(orc.n_ckpt[0]))
         if nk[-1] == nc[-1] and keep_ckpt(t):
             ck[t] = orc.S_ckpt[0].copy()
-    return dict(y=np.array(ys), nc=np.array(nc), nk=np.array(nk), ckpt=ck)
+    return dict(y=np.array(ys), nc=np.array(nc), nk=np.array(nk), ckpt=ck,
+                allowance=np.array(al) if al else None)
 
 
 def _spec_seq(args):

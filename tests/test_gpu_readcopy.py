@@ -10,8 +10,9 @@ from oracle import (ReplayOracle, dequantize_fp8_blocks, dequantize_mxfp4_blocks
 from synth import decode_inputs, get_workload, initial_state
 from synth.stream import StepSource
 
-from gpu_util import (TOL_READ, decode, dev, new_state, relerr, to_dev_inputs)
-from oracle_runs import decode_runs
+from gpu_util import (TOL, TOL_READ, decode, dev, new_state, read_copy_excess, relerr, tile_relerr,
+                      to_dev_inputs)
+from oracle_runs import READ_TOL, decode_runs
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +85,7 @@ def test_decode_with_read_copy_matches_oracle(fmt, shape):
     wl = _wl(fmt, dv=P, dk=N, in_dtype=dt, L=6, capacity=6)
     seqs = list(range(wl.batch))
     S0 = initial_state(wl, seqs)
-    orc = ReplayOracle(wl, seqs, S0)
+    orc = ReplayOracle(wl, seqs, S0, read_tol=READ_TOL)
     ds = new_state(wl, S0)
     plain = new_state(wl.replace(read_copy="none"), S0)
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
@@ -95,18 +96,29 @@ def test_decode_with_read_copy_matches_oracle(fmt, shape):
         decode(ds, d, y)
         decode(plain, d, y2)
         yr = orc.decode(inp)
-        err = relerr(y.cpu().numpy(), yr).max()
-        assert err <= TOL_READ, f"step {t}: rel err {err:.3g}"
+        got = y.cpu().numpy()
+        err = relerr(got, yr).max()
+        if fmt == "fp8":
+            assert err <= TOL_READ, f"step {t}: rel err {err:.3g}"
+        ex = read_copy_excess(got, yr, orc.allowance).max()
+        assert ex <= 0, f"step {t}: output outside fp32 tolerance + quantisation ambiguity by {ex:.3g}"
         # the copy never feeds the recurrence: checkpoints are bit-identical to the plain run
         assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32))
         if (t + 1) % wl.L == 0:
             assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+        if (t + 1) % wl.L == 0:
+            assert tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max() <= TOL
     assert ds.error() == 0
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 def test_serving_shape_read_copy_sampled(fmt):
-    """Mamba-2 serving shape (B=256, H=128, P=64, N=128, bf16) with a read copy, 512 steps."""
+    """Mamba-2 serving shape (B=256, H=128, P=64, N=128, bf16) with a read copy, 512 steps.
+
+    Each output row must match the oracle (which quantises its own fp32 checkpoint) to the fp32
+    tolerance plus the oracle's bound on what an element lying within that tolerance of a
+    rounding boundary may change; the normwise error is also held to 5e-2 for fp8 and reported
+    for MXFP4, where a single ambiguous E2M1 code moves a row by a few percent."""
     wl = get_workload("m2_readcopy_b256").replace(read_copy=fmt)
     steps = 512
     seqs = list(range(wl.batch))
@@ -117,13 +129,18 @@ def test_serving_shape_read_copy_sampled(fmt):
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
     idx = torch.tensor(sample, device="cuda")
     worst = 0.0
+    excess = -1.0
     with StepSource(wl, seqs) as src:
         for t in range(steps):
             decode(ds, to_dev_inputs(src.decode(t)), y)
             got = y[idx].cpu().numpy()
             for i, b in enumerate(sample):
                 worst = max(worst, relerr(got[i], ref[b]["y"][t]).max())
+                excess = max(excess, read_copy_excess(got[i], ref[b]["y"][t], ref[b]["allowance"][t]).max())
             if t % 128 == 127:
-                print(f"[read copy {fmt}] step {t + 1}/{steps} worst rel err {worst:.3g}", flush=True)
-    assert worst <= TOL_READ
+                print(f"[read copy {fmt}] step {t + 1}/{steps} worst normwise rel err {worst:.3g}, "
+                      f"worst excess over tolerance+ambiguity {excess:.3g}", flush=True)
+    assert excess <= 0
+    if fmt == "fp8":
+        assert worst <= TOL_READ
     assert ds.error() == 0

@@ -136,3 +136,28 @@ def test_mxfp4_packing_low_nibble_first():
     packed, e8 = quantize_mxfp4_blocks(x)
     assert e8[0, 0] == 125
     assert packed[0, 0] == (6 | (12 << 4))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_ambiguity_bound_covers_brute_force_perturbations(fmt):
+    """Random perturbations of the float32 input within +-delta never change a dequantised
+    value by more than read_copy_ambiguity's bound; delta = 0 gives a zero bound."""
+    from oracle import read_copy_ambiguity, read_copy_dequant
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((8, 64)) * 0.3).astype(np.float32)
+    x[0, :32] = np.float32(2.0) ** np.arange(-16, 16)       # block maxima on powers of two
+    x[1, 5] = np.float32(448.0)
+    delta = 2e-5 * np.max(np.abs(x), axis=-1, keepdims=True)      # per row, as per tile in use
+    bound = read_copy_ambiguity(fmt, x, delta)
+    assert np.all(read_copy_ambiguity(fmt, x, 0.0) == 0)
+    base = read_copy_dequant(fmt, x)
+    worst_seen = 0.0
+    for trial in range(300):
+        dx = rng.uniform(-delta, delta, x.shape)
+        if trial % 3 == 0:
+            dx = np.sign(dx) * delta                           # corners
+        xp = (x.astype(np.float64) + dx).astype(np.float32)
+        dev = np.abs(read_copy_dequant(fmt, xp) - base)
+        assert np.all(dev <= bound * (1 + 1e-12) + 1e-30)
+        worst_seen = max(worst_seen, float(np.max(dev)))
+    assert worst_seen > 0                                       # some perturbation did flip a code
