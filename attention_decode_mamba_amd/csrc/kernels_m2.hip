@@ -11,10 +11,19 @@ inline dim3 grid_of(const Args &a) { return dim3((unsigned)(a.g.B * a.g.H)); }
 
 hipError_t launch_decode_m2(const Args &a, hipStream_t s) {
   const size_t lds = lds_bytes(kKind, a.g.C + 1, 1, a.g.P, a.g.N);
-#define CALL(n, r)                                                                          \
-  {                                                                                         \
-    hipLaunchKernelGGL((k_decode<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);     \
-    return hipGetLastError();                                                               \
+  if (a.g.read_copy != RSSM_READ_NONE) {
+#define CALL(n, r)                                                                             \
+  {                                                                                            \
+    hipLaunchKernelGGL((k_decode<kKind, n, r, true>), grid_of(a), dim3(kThreads), lds, s, a);  \
+    return hipGetLastError();                                                                  \
+  }
+    RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+#undef CALL
+  }
+#define CALL(n, r)                                                                             \
+  {                                                                                            \
+    hipLaunchKernelGGL((k_decode<kKind, n, r, false>), grid_of(a), dim3(kThreads), lds, s, a); \
+    return hipGetLastError();                                                                  \
   }
   RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
 #undef CALL

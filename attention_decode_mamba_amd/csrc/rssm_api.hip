@@ -113,6 +113,15 @@ Args make_args(const rssm_config *c, const rssm_state *st) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
 
+// Rows can be moved in 16-byte chunks when a row is a whole number of chunks and every
+// input row starts on a 16-byte boundary (ring rows then do too: the ring is 256-aligned).
+int vec16_ok(const rssm_config *c, const void *v, const void *k, const void *q) {
+  const int epc = c->in_dtype == RSSM_DTYPE_BF16 ? 8 : 4;
+  if (c->dv % epc || c->dk % epc) return 0;
+  if ((v && !aligned(v, 16)) || (k && !aligned(k, 16)) || (q && !aligned(q, 16))) return 0;
+  return 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,6 +186,7 @@ int rssm_decode_step(const rssm_config *cfg, const rssm_state *st, const void *a
   a.k = k;
   a.q = q;
   a.out = y;
+  a.vec16 = vec16_ok(cfg, v, k, q);
   return hip_status(launch_decode(a, stream));
 }
 
@@ -188,6 +198,7 @@ int rssm_flush(const rssm_config *cfg, const rssm_state *st, int32_t min_records
   if (cfg->batch == 0) return RSSM_OK;
   Args a = make_args(cfg, st);
   a.min_records = min_records;
+  a.vec16 = vec16_ok(cfg, nullptr, nullptr, nullptr);
   return hip_status(launch_flush(a, stream));
 }
 
@@ -207,6 +218,7 @@ int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const v
   a.q = q;
   a.out = o;
   a.T = T;
+  a.vec16 = vec16_ok(cfg, v, k, q);
   return hip_status(launch_verify(a, stream));
 }
 
@@ -241,6 +253,7 @@ int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *
   a.k = k;
   a.q = q;
   a.out = y;
+  a.vec16 = vec16_ok(cfg, v, k, q);
   return hip_status(launch_conventional(a, stream));
 }
 

@@ -9,6 +9,12 @@
 // A row's N values are thus spread over 4 lanes (l/16 = 0..3) times N/16 registers,
 // so a row dot product is N/16 float4 FMAs per lane plus two cross-lane adds; and
 // the layout is the operand/accumulator layout of the 16x16x4 fp32 MFMA.
+//
+// Latency structure of every kernel: the cursor is read first; then all loads of
+// the ring records, step inputs and queries are issued (16-byte chunks), then the
+// loads of the checkpoint tile (or its read copy); the staged records are written
+// to LDS while the tile is still in flight, so one workgroup waits for one memory
+// round trip, not one per record.
 #pragma once
 
 #include "rssm_internal.hpp"
@@ -20,13 +26,6 @@ __device__ __forceinline__ float bf16f(uint16_t u) { return __uint_as_float(((ui
 
 __device__ __forceinline__ float ld_in(const void *base, int64_t i, int bf16) {
   return bf16 ? bf16f(((const uint16_t *)base)[i]) : ((const float *)base)[i];
-}
-
-__device__ __forceinline__ void cp_in(void *dst, int64_t di, const void *src, int64_t si, int bf16) {
-  if (bf16)
-    ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
-  else
-    ((float *)dst)[di] = ((const float *)src)[si];
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous
@@ -58,6 +57,16 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 2);
   v += __shfl_xor(v, 1);
   return v;
+}
+
+// x_l <- prod_{m >= l} x_m over the 64 lanes of the wave (all lanes must be active).
+__device__ __forceinline__ float wave_suffix_product(float x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_down(x, o);
+    if (lane + o < 64) x *= y;
+  }
+  return x;
 }
 
 // ---------------------------------------------------------------- fragments
@@ -121,15 +130,13 @@ __device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc)
 template <int N, int RBW>
 __device__ __forceinline__ void frag_dot(const Frag<N, RBW> &F, const float *x, int lane, float (&out)[RBW]) {
   const int c = (lane >> 4) * 4;
-  float4 xv[N / 16];
 #pragma unroll
-  for (int f = 0; f < N / 16; ++f) xv[f] = *(const float4 *)(x + 16 * f + c);
+  for (int i = 0; i < RBW; ++i) out[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    float acc = 0.f;
+  for (int f = 0; f < N / 16; ++f) {
+    const float4 xv = *(const float4 *)(x + 16 * f + c);
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) acc = dot4(F.s[i][f], xv[f], acc);
-    out[i] = acc;
+    for (int i = 0; i < RBW; ++i) out[i] = dot4(F.s[i][f], xv, out[i]);
   }
 }
 
@@ -222,44 +229,59 @@ __device__ void frag_store_read_copy(const Frag<N, RBW> &F, int fmt, uint8_t *__
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-// Per-lane partial of S_read x from the read copy (non-flush steps).
-// fp8: lane handles 16-byte chunks (16 codes) ch = l/16 + 4*ci of its row;
-// MXFP4: 16-byte chunks of 32 codes (one block each).
+// Read-copy registers of the lane's rows: fp8 lanes take 16-byte chunks (16 codes)
+// ch = l/16 + 4*ci of a row; MXFP4 lanes take 16-byte chunks of 32 codes (one block).
 template <int N, int RBW>
-__device__ __forceinline__ void readcopy_dot(int fmt, const uint8_t *__restrict__ codes,
-                                             const uint8_t *__restrict__ scales, int64_t tile, const float *x,
-                                             int P, int wave, int lane, float (&out)[RBW]) {
+struct RCopy {
+  static constexpr int NCH = N / 16;            // fp8 chunks per row (MXFP4 uses N / 32)
+  static constexpr int CI = (NCH + 3) / 4;
+  uint4 raw[RBW][CI];
+  float sc[RBW][CI];
+};
+
+template <int N, int RBW>
+__device__ __forceinline__ void readcopy_load(RCopy<N, RBW> &R, int fmt, const uint8_t *__restrict__ codes,
+                                              const uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
+                                              int lane) {
   const int s = lane >> 4;
-  if (fmt == RSSM_READ_FP8) {
-    constexpr int NCH = N / 16;
-    constexpr int CI = (NCH + 3) / 4;
-    uint4 raw[RBW][CI];
-    float sc[RBW][CI];
+  const int nch = fmt == RSSM_READ_FP8 ? N / 16 : N / 32;
+  const int rowbytes = fmt == RSSM_READ_FP8 ? N : N / 2;
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      const int row = frag_row(wave, lane, i);
-      const int64_t rowi = tile * P + row;
+  for (int i = 0; i < RBW; ++i) {
+    const int row = frag_row(wave, lane, i);
+    const int64_t rowi = tile * P + row;
 #pragma unroll
-      for (int ci = 0; ci < CI; ++ci) {
-        const int ch = s + 4 * ci;
-        if (row < P && ch < NCH) {
-          raw[i][ci] = *(const uint4 *)(codes + rowi * N + 16 * ch);
-          sc[i][ci] = ((const float *)scales)[rowi * (N / 32) + ch / 2];
-        } else {
-          raw[i][ci] = make_uint4(0, 0, 0, 0);
-          sc[i][ci] = 0.f;
-        }
+    for (int ci = 0; ci < RCopy<N, RBW>::CI; ++ci) {
+      const int ch = s + 4 * ci;
+      if (row < P && ch < nch) {
+        R.raw[i][ci] = *(const uint4 *)(codes + rowi * rowbytes + 16 * ch);
+        if (fmt == RSSM_READ_FP8)
+          R.sc[i][ci] = ((const float *)scales)[rowi * (N / 32) + ch / 2];
+        else
+          R.sc[i][ci] = __uint_as_float((uint32_t)scales[rowi * (N / 32) + ch] << 23);   // 2^(e8m0 - 127)
+      } else {
+        R.raw[i][ci] = make_uint4(0, 0, 0, 0);
+        R.sc[i][ci] = 0.f;
       }
     }
+  }
+}
+
+// Per-lane partial of S_read x from loaded read-copy registers.
+template <int N, int RBW>
+__device__ __forceinline__ void readcopy_dot(const RCopy<N, RBW> &R, int fmt, const float *x, int lane,
+                                             float (&out)[RBW]) {
+  const int s = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      float acc = 0.f;
+  for (int i = 0; i < RBW; ++i) {
+    float acc = 0.f;
 #pragma unroll
-      for (int ci = 0; ci < CI; ++ci) {
-        const int ch = s + 4 * ci;
-        if (ch < NCH) {
+    for (int ci = 0; ci < RCopy<N, RBW>::CI; ++ci) {
+      const int ch = s + 4 * ci;
+      const uint32_t w[4] = {R.raw[i][ci].x, R.raw[i][ci].y, R.raw[i][ci].z, R.raw[i][ci].w};
+      if (fmt == RSSM_READ_FP8) {
+        if (ch < N / 16) {
           const float *xp = x + 16 * ch;
-          const uint32_t w[4] = {raw[i][ci].x, raw[i][ci].y, raw[i][ci].z, raw[i][ci].w};
           float d = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -271,49 +293,20 @@ __device__ __forceinline__ void readcopy_dot(int fmt, const uint8_t *__restrict_
             d = fmaf(hi[0], xv.z, d);
             d = fmaf(hi[1], xv.w, d);
           }
-          acc = fmaf(sc[i][ci], d, acc);
+          acc = fmaf(R.sc[i][ci], d, acc);
         }
-      }
-      out[i] = acc;
-    }
-  } else {
-    constexpr int NCH = N / 32;
-    constexpr int CI = (NCH + 3) / 4;
-    uint4 raw[RBW][CI];
-    float sc[RBW][CI];
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      const int row = frag_row(wave, lane, i);
-      const int64_t rowi = tile * P + row;
-#pragma unroll
-      for (int ci = 0; ci < CI; ++ci) {
-        const int ch = s + 4 * ci;
-        if (row < P && ch < NCH) {
-          raw[i][ci] = *(const uint4 *)(codes + rowi * (N / 2) + 16 * ch);
-          sc[i][ci] = __uint_as_float((uint32_t)scales[rowi * (N / 32) + ch] << 23);   // 2^(e8m0 - 127)
-        } else {
-          raw[i][ci] = make_uint4(0, 0, 0, 0);
-          sc[i][ci] = 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int ci = 0; ci < CI; ++ci) {
-        const int ch = s + 4 * ci;
-        if (ch < NCH) {
+      } else {
+        if (ch < N / 32) {
           const float *xp = x + 32 * ch;
-          const uint32_t w[4] = {raw[i][ci].x, raw[i][ci].y, raw[i][ci].z, raw[i][ci].w};
+          const float sc = R.sc[i][ci];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 xa = *(const float4 *)(xp + 8 * q);
             const float4 xb = *(const float4 *)(xp + 8 * q + 4);
-            const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc[i][ci], 0);
-            const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc[i][ci], 1);
-            const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc[i][ci], 2);
-            const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc[i][ci], 3);
+            const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 0);
+            const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 1);
+            const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 2);
+            const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 3);
             acc = fmaf(v0[0], xa.x, acc);
             acc = fmaf(v0[1], xa.y, acc);
             acc = fmaf(v1[0], xa.z, acc);
@@ -325,125 +318,304 @@ __device__ __forceinline__ void readcopy_dot(int fmt, const uint8_t *__restrict_
           }
         }
       }
-      out[i] = acc;
     }
+    out[i] = acc;
   }
 }
 
 // ---------------------------------------------------------------- record staging
-// Record j < n_ring comes from ring slot (start + j) % C; record j in [n_ring, n_ring + n_in)
-// is input record j - n_ring at the given element offsets and strides.
-struct RecSrc {
-  int n_ring;
-  int n_in;
-  int slot0;        // start % C
-  int64_t a_idx, a_str;
-  int64_t v_idx, v_str;
-  int64_t k_idx, k_str;
+// Records j < n_ring come from ring slot (slot0 + j) % C; records j in [n_ring, nrec)
+// are input records j - n_ring (element offsets iv0/ik0 + (j - n_ring) * stride).
+// Queries are nq input rows (iq0 + r * iqs).  Everything lands in LDS as fp32:
+// alpha[j], beta[j], V[j][P], K[j][N+4], Q[r][N].
+struct StageSpec {
+  int nrec, n_ring, slot0, C, P, N, nq, bf16;
+  const uint8_t *rA, *rB, *rV, *rK;      // ring regions
+  int64_t hrow, krow;                    // ring row (slot 0) of this value head / key head
+  const void *iA, *iB, *iV, *iK, *iQ;    // inputs
+  int64_t ia0, ias, iv0, ivs, ik0, iks, iq0, iqs;
+  float *A, *Bt, *V, *K, *Q;             // LDS
 };
 
-template <int KIND, int N>
-__device__ void stage_records(const Args &a, const LdsLayout &L, float *lds, int b, int hh, int gq,
-                              const RecSrc &rs, int t) {
-  const Geom &g = a.g;
-  const int bf = g.bf16;
-  const int nrec = rs.n_ring + rs.n_in;
-  const int P = g.P;
-  const uint8_t *rA = a.ring + g.off_alpha;
-  const uint8_t *rB = a.ring + g.off_beta;
-  const uint8_t *rV = a.ring + g.off_v;
-  const uint8_t *rK = a.ring + g.off_k;
-  const int64_t hrow = (int64_t)(b * g.H + hh) * g.C;   // alpha/beta/v ring row of this value head
-  const int64_t krow = (int64_t)(b * g.G + gq) * g.C;   // k ring row of this key head
-  for (int j = t; j < nrec; j += kThreads) {
-    float al, be = 0.f;
-    if (j < rs.n_ring) {
-      int slot = rs.slot0 + j;
-      if (slot >= g.C) slot -= g.C;
-      al = ld_in(rA, hrow + slot, bf);
-      if (KIND == RSSM_KIND_GDN) be = ld_in(rB, hrow + slot, bf);
-    } else {
-      const int64_t i = rs.a_idx + (int64_t)(j - rs.n_ring) * rs.a_str;
-      al = ld_in(a.alpha, i, bf);
-      if (KIND == RSSM_KIND_GDN) be = ld_in(a.beta, i, bf);
+__device__ __forceinline__ int ring_slot(const StageSpec &sp, int j) {
+  int s = sp.slot0 + j;
+  return s >= sp.C ? s - sp.C : s;
+}
+
+// Vectorised staging: 16-byte chunks (8 bf16 or 4 fp32 elements), U chunks per thread
+// per round.  stage_issue() loads one round into registers, stage_commit() writes it.
+template <int U>
+struct StageRegs {
+  uint4 raw[U];
+  int dst[U];        // LDS float offset of the chunk, -1 when idle
+  float a, b;        // alpha / beta of record t (thread t < nrec)
+};
+
+__device__ __forceinline__ int stage_chunks(const StageSpec &sp, int epc) {
+  return sp.nrec * (sp.P / epc) + sp.nrec * (sp.N / epc) + sp.nq * (sp.N / epc);
+}
+
+template <int U>
+__device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R, int base, float *lds, int t,
+                                            bool with_scalars) {
+  const int es = sp.bf16 ? 2 : 4;
+  const int epc = 16 / es;
+  const int cpv = sp.P / epc, cpk = sp.N / epc;
+  const int nV = sp.nrec * cpv, nK = sp.nrec * cpk, total = nV + nK + sp.nq * cpk;
+  if (with_scalars) {
+    R.a = 0.f;
+    R.b = 0.f;
+    if (t < sp.nrec) {
+      if (t < sp.n_ring) {
+        const int64_t i = sp.hrow + ring_slot(sp, t);
+        R.a = ld_in(sp.rA, i, sp.bf16);
+        if (sp.rB) R.b = ld_in(sp.rB, i, sp.bf16);
+      } else {
+        const int64_t i = sp.ia0 + (int64_t)(t - sp.n_ring) * sp.ias;
+        R.a = ld_in(sp.iA, i, sp.bf16);
+        if (sp.iB) R.b = ld_in(sp.iB, i, sp.bf16);
+      }
     }
-    lds[L.alpha + j] = al;
-    lds[L.beta + j] = be;
   }
-  for (int e = t; e < nrec * P; e += kThreads) {
-    const int j = e / P, p = e - j * P;
-    float x;
-    if (j < rs.n_ring) {
-      int slot = rs.slot0 + j;
-      if (slot >= g.C) slot -= g.C;
-      x = ld_in(rV, (hrow + slot) * P + p, bf);
-    } else {
-      x = ld_in(a.v, rs.v_idx + (int64_t)(j - rs.n_ring) * rs.v_str + p, bf);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = base + u * kThreads + t;
+    R.dst[u] = -1;
+    R.raw[u] = make_uint4(0, 0, 0, 0);
+    if (c < total) {
+      const uint8_t *src;
+      if (c < nV) {
+        const int j = c / cpv, e = (c - j * cpv) * epc;
+        src = j < sp.n_ring ? sp.rV + ((sp.hrow + ring_slot(sp, j)) * sp.P + e) * es
+                            : (const uint8_t *)sp.iV + (sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + e) * es;
+        R.dst[u] = (int)(sp.V - lds) + j * sp.P + e;
+      } else if (c < nV + nK) {
+        const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
+        src = j < sp.n_ring ? sp.rK + ((sp.krow + ring_slot(sp, j)) * sp.N + e) * es
+                            : (const uint8_t *)sp.iK + (sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + e) * es;
+        R.dst[u] = (int)(sp.K - lds) + j * (sp.N + 4) + e;
+      } else {
+        const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
+        src = (const uint8_t *)sp.iQ + (sp.iq0 + (int64_t)r * sp.iqs + e) * es;
+        R.dst[u] = (int)(sp.Q - lds) + r * sp.N + e;
+      }
+      R.raw[u] = *(const uint4 *)src;
     }
-    lds[L.V + e] = x;
-  }
-  for (int e = t; e < nrec * N; e += kThreads) {
-    const int j = e / N, n = e % N;
-    float x;
-    if (j < rs.n_ring) {
-      int slot = rs.slot0 + j;
-      if (slot >= g.C) slot -= g.C;
-      x = ld_in(rK, (krow + slot) * N + n, bf);
-    } else {
-      x = ld_in(a.k, rs.k_idx + (int64_t)(j - rs.n_ring) * rs.k_str + n, bf);
-    }
-    lds[L.K + j * (N + 4) + n] = x;
   }
 }
 
-// Append input record r (0-based) of the given source layout to ring slot `slot`.
+template <int U>
+__device__ __forceinline__ void stage_commit(const StageSpec &sp, const StageRegs<U> &R, float *lds, int t,
+                                             bool with_scalars) {
+  if (with_scalars && t < sp.nrec) {
+    sp.A[t] = R.a;
+    sp.Bt[t] = R.b;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (R.dst[u] < 0) continue;
+    float *d = lds + R.dst[u];
+    const uint4 w = R.raw[u];
+    if (sp.bf16) {
+      *(float4 *)d = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      *(float4 *)(d + 4) = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                                       __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u));
+    } else {
+      *(float4 *)d = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                 __uint_as_float(w.w));
+    }
+  }
+}
+
+// Element-wise staging for shapes that cannot use 16-byte chunks (e.g. P % 8 != 0 with bf16).
+__device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
+  for (int j = t; j < sp.nrec; j += kThreads) {
+    float al, be = 0.f;
+    if (j < sp.n_ring) {
+      const int64_t i = sp.hrow + ring_slot(sp, j);
+      al = ld_in(sp.rA, i, sp.bf16);
+      if (sp.rB) be = ld_in(sp.rB, i, sp.bf16);
+    } else {
+      const int64_t i = sp.ia0 + (int64_t)(j - sp.n_ring) * sp.ias;
+      al = ld_in(sp.iA, i, sp.bf16);
+      if (sp.iB) be = ld_in(sp.iB, i, sp.bf16);
+    }
+    sp.A[j] = al;
+    sp.Bt[j] = be;
+  }
+  for (int e = t; e < sp.nrec * sp.P; e += kThreads) {
+    const int j = e / sp.P, p = e - j * sp.P;
+    sp.V[e] = j < sp.n_ring ? ld_in(sp.rV, (sp.hrow + ring_slot(sp, j)) * sp.P + p, sp.bf16)
+                            : ld_in(sp.iV, sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + p, sp.bf16);
+  }
+  for (int e = t; e < sp.nrec * sp.N; e += kThreads) {
+    const int j = e / sp.N, n = e - j * sp.N;
+    sp.K[j * (sp.N + 4) + n] = j < sp.n_ring ? ld_in(sp.rK, (sp.krow + ring_slot(sp, j)) * sp.N + n, sp.bf16)
+                                             : ld_in(sp.iK, sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + n, sp.bf16);
+  }
+  for (int e = t; e < sp.nq * sp.N; e += kThreads) {
+    const int r = e / sp.N, n = e - r * sp.N;
+    sp.Q[e] = ld_in(sp.iQ, sp.iq0 + (int64_t)r * sp.iqs + n, sp.bf16);
+  }
+}
+
+// Common record source description of a tile.
 template <int KIND, int N>
-__device__ void append_record(const Args &a, int b, int hh, int gq, int slot, int64_t a_i, int64_t v_i,
-                              int64_t k_i, int t) {
+__device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L, float *lds, int b, int hh,
+                                               int gq, int64_t nk, int n_ring, int n_in, int nq) {
   const Geom &g = a.g;
-  const int bf = g.bf16;
+  StageSpec sp;
+  sp.nrec = n_ring + n_in;
+  sp.n_ring = n_ring;
+  sp.slot0 = (int)(nk % g.C);
+  sp.C = g.C;
+  sp.P = g.P;
+  sp.N = N;
+  sp.nq = nq;
+  sp.bf16 = g.bf16;
+  sp.rA = a.ring + g.off_alpha;
+  sp.rB = KIND == RSSM_KIND_GDN ? a.ring + g.off_beta : nullptr;
+  sp.rV = a.ring + g.off_v;
+  sp.rK = a.ring + g.off_k;
+  sp.hrow = (int64_t)(b * g.H + hh) * g.C;
+  sp.krow = (int64_t)(b * g.G + gq) * g.C;
+  sp.iA = a.alpha;
+  sp.iB = KIND == RSSM_KIND_GDN ? a.beta : nullptr;
+  sp.iV = a.v;
+  sp.iK = a.k;
+  sp.iQ = a.q;
+  sp.ia0 = sp.ias = sp.iv0 = sp.ivs = sp.ik0 = sp.iks = sp.iq0 = sp.iqs = 0;
+  sp.A = lds + L.alpha;
+  sp.Bt = lds + L.beta;
+  sp.V = lds + L.V;
+  sp.K = lds + L.K;
+  sp.Q = lds + L.q;
+  return sp;
+}
+
+// Stage a tile's records with the checkpoint loads in flight: record loads are issued
+// first, then `issue_tile()` (the checkpoint or read-copy loads), then the LDS writes.
+template <int U, class IssueTile>
+__device__ __forceinline__ void stage_with_tile(const Args &a, const StageSpec &sp, float *lds, int t,
+                                                IssueTile &&issue_tile) {
+  if (a.vec16) {
+    StageRegs<U> SR;
+    stage_issue(sp, SR, 0, lds, t, true);
+    issue_tile();
+    stage_commit(sp, SR, lds, t, true);
+    const int total = stage_chunks(sp, sp.bf16 ? 8 : 4);
+    for (int base = kThreads * U; base < total; base += kThreads * U) {
+      stage_issue(sp, SR, base, lds, t, false);
+      stage_commit(sp, SR, lds, t, false);
+    }
+  } else {
+    issue_tile();
+    stage_scalar(sp, t);
+  }
+}
+
+// Append record row j of LDS (and query row qr) to ring slot `slot` (values are exact
+// widenings of the inputs, so narrowing back to bf16 reproduces the input bits).
+template <int KIND, int N>
+__device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *lds, int b, int hh, int gq, int j,
+                                int qr, int slot, int t) {
+  const Geom &g = a.g;
   const int P = g.P;
   const int64_t hr = (int64_t)(b * g.H + hh) * g.C + slot;
-  if (t == 0) {
-    cp_in(a.ring + g.off_alpha, hr, a.alpha, a_i, bf);
-    if (KIND == RSSM_KIND_GDN) cp_in(a.ring + g.off_beta, hr, a.beta, a_i, bf);
-  }
-  for (int p = t; p < P; p += kThreads) cp_in(a.ring + g.off_v, hr * P + p, a.v, v_i + p, bf);
-  if (hh % g.grp == 0) {
-    const int64_t kr = ((int64_t)(b * g.G + gq) * g.C + slot) * N;
-    for (int n = t; n < N; n += kThreads) {
-      cp_in(a.ring + g.off_k, kr + n, a.k, k_i + n, bf);
-      cp_in(a.ring + g.off_q, kr + n, a.q, k_i + n, bf);
+  const bool lead = (hh % g.grp) == 0;
+  const int64_t kr = ((int64_t)(b * g.G + gq) * g.C + slot) * N;
+  if (g.bf16) {
+    uint16_t *rA = (uint16_t *)(a.ring + g.off_alpha);
+    uint16_t *rV = (uint16_t *)(a.ring + g.off_v);
+    uint16_t *rK = (uint16_t *)(a.ring + g.off_k);
+    uint16_t *rQ = (uint16_t *)(a.ring + g.off_q);
+    if (t == 0) {
+      rA[hr] = (uint16_t)(__float_as_uint(lds[L.alpha + j]) >> 16);
+      if (KIND == RSSM_KIND_GDN)
+        ((uint16_t *)(a.ring + g.off_beta))[hr] = (uint16_t)(__float_as_uint(lds[L.beta + j]) >> 16);
     }
+    if (a.vec16) {
+      // 8 elements per 16-byte store: v (P/8 chunks), then k and q (N/8 each, key-head leader only)
+      const int cv = P / 8, ck = N / 8;
+      const int total = cv + (lead ? 2 * ck : 0);
+      for (int c = t; c < total; c += kThreads) {
+        const float *src;
+        uint16_t *dst;
+        if (c < cv) {
+          src = lds + L.V + j * P + 8 * c;
+          dst = rV + hr * P + 8 * c;
+        } else if (c < cv + ck) {
+          src = lds + L.K + j * (N + 4) + 8 * (c - cv);
+          dst = rK + kr + 8 * (c - cv);
+        } else {
+          src = lds + L.q + qr * N + 8 * (c - cv - ck);
+          dst = rQ + kr + 8 * (c - cv - ck);
+        }
+        const float4 x0 = *(const float4 *)src, x1 = *(const float4 *)(src + 4);
+        uint4 w;
+        w.x = (__float_as_uint(x0.x) >> 16) | (__float_as_uint(x0.y) & 0xFFFF0000u);
+        w.y = (__float_as_uint(x0.z) >> 16) | (__float_as_uint(x0.w) & 0xFFFF0000u);
+        w.z = (__float_as_uint(x1.x) >> 16) | (__float_as_uint(x1.y) & 0xFFFF0000u);
+        w.w = (__float_as_uint(x1.z) >> 16) | (__float_as_uint(x1.w) & 0xFFFF0000u);
+        *(uint4 *)dst = w;
+      }
+    } else {
+      for (int p = t; p < P; p += kThreads) rV[hr * P + p] = (uint16_t)(__float_as_uint(lds[L.V + j * P + p]) >> 16);
+      if (lead)
+        for (int n = t; n < N; n += kThreads) {
+          rK[kr + n] = (uint16_t)(__float_as_uint(lds[L.K + j * (N + 4) + n]) >> 16);
+          rQ[kr + n] = (uint16_t)(__float_as_uint(lds[L.q + qr * N + n]) >> 16);
+        }
+    }
+  } else {
+    float *rA = (float *)(a.ring + g.off_alpha);
+    float *rV = (float *)(a.ring + g.off_v);
+    float *rK = (float *)(a.ring + g.off_k);
+    float *rQ = (float *)(a.ring + g.off_q);
+    if (t == 0) {
+      rA[hr] = lds[L.alpha + j];
+      if (KIND == RSSM_KIND_GDN) ((float *)(a.ring + g.off_beta))[hr] = lds[L.beta + j];
+    }
+    for (int p = t; p < P; p += kThreads) rV[hr * P + p] = lds[L.V + j * P + p];
+    if (lead)
+      for (int n = t; n < N; n += kThreads) {
+        rK[kr + n] = lds[L.K + j * (N + 4) + n];
+        rQ[kr + n] = lds[L.q + qr * N + n];
+      }
   }
 }
 
 // ---------------------------------------------------------------- coefficient phases
-// d_j = prod_{j < m < nrec} alpha_m and G = prod_{m < nrec} alpha_m (records since the checkpoint).
-__device__ __forceinline__ float suffix_decay(const float *alpha, int j, int last) {
-  float d = 1.f;
-  for (int m = last; m > j; --m) d *= alpha[m];
-  return d;
+// Decays of one query over records 0..last (one wave, all lanes active):
+// dec[j] = prod_{j < m <= last} alpha_m for j <= last and 0 for last < j < cap;
+// *gam = prod_{m <= last} alpha_m.
+__device__ __forceinline__ void wave_decays(const float *alpha, int last, float *dec, float *gam, int cap,
+                                            int lane) {
+  float x = (lane <= last) ? alpha[lane] : 1.f;
+  x = wave_suffix_product(x, lane);
+  const float nxt = __shfl_down(x, 1);
+  if (lane < cap) dec[lane] = (lane < last) ? nxt : (lane == last ? 1.f : 0.f);
+  if (lane == 0) *gam = x;
 }
 
-// Mamba-2: e_j = d_j (k_j . x) for the nrec records, and G, for one query x.
+// Dot products k_j . q_tau for j < nrec, tau < T, by groups of 16 lanes -> coef[tau * cap + j].
 template <int N>
-__device__ void coef_m2(float *lds, const LdsLayout &L, int nrec, const float *x, float *coef, float *gam,
-                        int t) {
+__device__ void kq_dots(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
   const int g16 = t >> 4, l16 = t & 15;
-  const float *alpha = lds + L.alpha;
-  for (int d = g16; d < nrec; d += kThreads / 16) {
-    const float *kr = lds + L.K + d * (N + 4);
+  for (int d = g16; d < T * nrec; d += kThreads / 16) {
+    const int tau = d / nrec, j = d - tau * nrec;
+    const float *kr = lds + L.K + j * (N + 4);
+    const float *qr = lds + L.q + tau * N;
     float acc = 0.f;
 #pragma unroll
-    for (int n = l16; n < N; n += 16) acc = fmaf(kr[n], x[n], acc);
+    for (int n = l16; n < N; n += 16) acc = fmaf(kr[n], qr[n], acc);
     acc = sum16(acc);
-    if (l16 == 0) coef[d] = suffix_decay(alpha, d, nrec - 1) * acc;
+    if (l16 == 0) lds[L.coef + tau * cap + j] = acc;
   }
-  if (t == 0) *gam = suffix_decay(alpha, -1, nrec - 1);
 }
 
-// Gated DeltaNet: Gram matrix K^T K (i < m) and K^T x for T queries over nrec records.
+// Gated DeltaNet: Gram matrix K^T K (i < m) and K^T q_tau for T queries over nrec records.
 template <int N>
 __device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
   const int g16 = t >> 4, l16 = t & 15;
@@ -480,7 +652,7 @@ __device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, i
 
 // Query-transform solve for one query over records 0..n-1 (one wave; n <= 64):
 // c_i = k_i . q - sum_{m > i} b_m c_m (k_i . k_m); writes c (cc row), e_i = d_i b_i c_i
-// (coef row, replacing k_i . q) and the decay product G.
+// (coef row, replacing k_i . q) with d_i = prod_{i < m < n} alpha_m, and G.
 __device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane) {
   const float *alpha = lds + L.alpha;
   const float *beta = lds + L.beta;
@@ -492,11 +664,14 @@ __device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, i
     const float cm = __shfl(x, m);
     if (lane < m) x = fmaf(-beta[m] * cm, gram[lane * (cap + 1) + m], x);
   }
+  float p = (lane < n) ? alpha[lane] : 1.f;
+  p = wave_suffix_product(p, lane);
+  const float d = __shfl_down(p, 1);
   if (lane < n) {
     cc[lane] = x;
-    coef[lane] = suffix_decay(alpha, lane, n - 1) * beta[lane] * x;
+    coef[lane] = (lane == n - 1 ? 1.f : d) * beta[lane] * x;
   }
-  if (lane == 0) lds[L.gam + tau] = suffix_decay(alpha, -1, n - 1);
+  if (lane == 0) lds[L.gam + tau] = p;
 }
 
 // r = q - sum_{i < n} b_i c_i k_i for query tau (threads stride over N).
@@ -530,19 +705,21 @@ __device__ void fold_m2(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, i
   for (int j = 0; j < nrec; ++j) {
     const float dj = lds[L.dec + j];
     const float *kr = lds + L.K + j * (N + 4) + c;
-    float4 kf[N / 16];
-#pragma unroll
-    for (int f = 0; f < N / 16; ++f) kf[f] = *(const float4 *)(kr + 16 * f);
+    float vr[RBW];
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
       const int row = frag_row(wave, lane, i);
-      const float vr = (row < P) ? lds[L.V + j * P + row] * dj : 0.f;
+      vr[i] = (row < P) ? lds[L.V + j * P + row] * dj : 0.f;
+    }
 #pragma unroll
-      for (int f = 0; f < N / 16; ++f) {
-        F.s[i][f].x = fmaf(vr, kf[f].x, F.s[i][f].x);
-        F.s[i][f].y = fmaf(vr, kf[f].y, F.s[i][f].y);
-        F.s[i][f].z = fmaf(vr, kf[f].z, F.s[i][f].z);
-        F.s[i][f].w = fmaf(vr, kf[f].w, F.s[i][f].w);
+    for (int f = 0; f < N / 16; ++f) {
+      const float4 kf = *(const float4 *)(kr + 16 * f);
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        F.s[i][f].x = fmaf(vr[i], kf.x, F.s[i][f].x);
+        F.s[i][f].y = fmaf(vr[i], kf.y, F.s[i][f].y);
+        F.s[i][f].z = fmaf(vr[i], kf.z, F.s[i][f].z);
+        F.s[i][f].w = fmaf(vr[i], kf.w, F.s[i][f].w);
       }
     }
   }
@@ -557,41 +734,54 @@ __device__ void fold_gdn(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, 
   for (int j = 0; j < nrec; ++j) {
     const float al = lds[L.alpha + j], be = lds[L.beta + j];
     const float *kr = lds + L.K + j * (N + 4) + c;
-    float4 kf[N / 16];
+    float w[RBW];
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) kf[f] = *(const float4 *)(kr + 16 * f);
+    for (int i = 0; i < RBW; ++i) w[i] = 0.f;
+#pragma unroll
+    for (int f = 0; f < N / 16; ++f) {
+      const float4 kf = *(const float4 *)(kr + 16 * f);
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
+    }
+    float u[RBW];
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
-      float w = 0.f;
-#pragma unroll
-      for (int f = 0; f < N / 16; ++f) w = dot4(F.s[i][f], kf[f], w);
-      w = quad_sum(w);
+      const float wi = quad_sum(w[i]);
       const int row = frag_row(wave, lane, i);
       const float vr = (row < P) ? lds[L.V + j * P + row] : 0.f;
-      const float u = be * (vr - al * w);
+      u[i] = be * (vr - al * wi);
+    }
 #pragma unroll
-      for (int f = 0; f < N / 16; ++f) {
-        F.s[i][f].x = fmaf(al, F.s[i][f].x, u * kf[f].x);
-        F.s[i][f].y = fmaf(al, F.s[i][f].y, u * kf[f].y);
-        F.s[i][f].z = fmaf(al, F.s[i][f].z, u * kf[f].z);
-        F.s[i][f].w = fmaf(al, F.s[i][f].w, u * kf[f].w);
+    for (int f = 0; f < N / 16; ++f) {
+      const float4 kf = *(const float4 *)(kr + 16 * f);
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
+        F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
+        F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
+        F.s[i][f].w = fmaf(al, F.s[i][f].w, u[i] * kf.w);
       }
     }
   }
 }
 
-// Output rows: y[row] = G * (S x)[row] + sum_{j} coef[j] v_j[row]; lanes with l/16 = s take j = s mod 4.
+// Output rows: y[row] = G * (S x)[row] + sum_{j < n} w_j v_j[row], where w_j = dec[j] * coef[j]
+// (Mamba-2: decay times k_j . q) or w_j = coef[j] (GDN: already d_j b_j c_j; dec == null).
+// Lanes with l/16 = s take records j = s mod 4.
 template <int RBW>
 __device__ __forceinline__ void write_rows(const float (&part)[RBW], float G, const float *lds, const LdsLayout &L,
-                                           const float *coef, int nrec, int P, float *__restrict__ out, int wave,
-                                           int lane) {
+                                           const float *dec, const float *coef, int n, int P,
+                                           float *__restrict__ out, int wave, int lane) {
   const int s = lane >> 4;
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
     const int row = frag_row(wave, lane, i);
     float buf = 0.f;
     if (row < P)
-      for (int j = s; j < nrec; j += 4) buf = fmaf(coef[j], lds[L.V + j * P + row], buf);
+      for (int j = s; j < n; j += 4) {
+        const float w = dec ? dec[j] * coef[j] : coef[j];
+        buf = fmaf(w, lds[L.V + j * P + row], buf);
+      }
     const float y = quad_sum(fmaf(G, part[i], buf));
     if (s == 0 && row < P) out[row] = y;
   }
@@ -599,8 +789,11 @@ __device__ __forceinline__ void write_rows(const float (&part)[RBW], float G, co
 
 // ================================================================ kernels
 
-template <int KIND, int N, int RBW>
+// U: staging chunks per thread per round (2 covers a 17-record Mamba-2 window at 64 x 128
+// in bf16 in one round).  RC: the kernel serves non-fold steps from the read copy.
+template <int KIND, int N, int RBW, bool RC>
 __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
+  constexpr int U = (KIND == RSSM_KIND_GDN || RBW > 1) ? 4 : 2;
   extern __shared__ float lds[];
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
@@ -618,37 +811,35 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   const int cap = g.C + 1;
   const LdsLayout L = lds_layout(KIND, cap, 1, P, N);
   float *tileS = a.s + (int64_t)tile * P * N;
-  const bool from_copy = (g.read_copy != RSSM_READ_NONE) && !flush;
+  const bool from_copy = RC && !flush;
+
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, 1, 1);
+  sp.ia0 = (int64_t)b * g.H + hh;
+  sp.iv0 = ((int64_t)b * g.H + hh) * P;
+  sp.ik0 = ((int64_t)b * g.G + gq) * N;
+  sp.iq0 = sp.ik0;
 
   Frag<N, RBW> F;
-  if (!from_copy) frag_load(F, tileS, P, wave, lane);
-
-  RecSrc rs;
-  rs.n_ring = hb;
-  rs.n_in = 1;
-  rs.slot0 = (int)(nk % g.C);
-  rs.a_idx = (int64_t)b * g.H + hh;
-  rs.a_str = 0;
-  rs.v_idx = ((int64_t)b * g.H + hh) * P;
-  rs.v_str = 0;
-  rs.k_idx = ((int64_t)b * g.G + gq) * N;
-  rs.k_str = 0;
-  stage_records<KIND, N>(a, L, lds, b, hh, gq, rs, t);
-  for (int n = t; n < N; n += kThreads) lds[L.q + n] = ld_in(a.q, rs.k_idx + n, g.bf16);
+  RCopy<N, RBW> RCR;
+  stage_with_tile<U>(a, sp, lds, t, [&]() {
+    if (from_copy)
+      readcopy_load(RCR, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+    else
+      frag_load(F, tileS, P, wave, lane);
+  });
   __syncthreads();
 
   float *yout = a.out + ((int64_t)b * g.H + hh) * P;
   if (flush) {
     if (KIND == RSSM_KIND_MAMBA2) {
-      for (int j = t; j < nrec; j += kThreads) lds[L.dec + j] = suffix_decay(lds + L.alpha, j, nrec - 1);
-      if (t == 0) lds[L.gam] = suffix_decay(lds + L.alpha, -1, nrec - 1);
+      if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
       __syncthreads();
       fold_m2(F, lds, L, nrec, P, wave, lane);
     } else {
       fold_gdn(F, lds, L, nrec, P, wave, lane);
     }
     frag_store(F, tileS, P, wave, lane);
-    if (g.read_copy != RSSM_READ_NONE) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+    if (RC) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
     float part[RBW];
     frag_dot(F, lds + L.q, lane, part);
 #pragma unroll
@@ -659,10 +850,13 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     }
   } else {
     const float *x;
+    const float *dec = nullptr;
     if (KIND == RSSM_KIND_MAMBA2) {
-      coef_m2<N>(lds, L, nrec, lds + L.q, lds + L.coef, lds + L.gam, t);
+      if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
+      kq_dots<N>(lds, L, cap, nrec, 1, t);
       __syncthreads();
       x = lds + L.q;
+      dec = lds + L.dec;
     } else {
       gram_and_kq<N>(lds, L, cap, nrec, 1, t);
       __syncthreads();
@@ -674,11 +868,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     }
     float part[RBW];
     if (from_copy)
-      readcopy_dot<N, RBW>(g.read_copy, a.s_read, a.s_read_scale, tile, x, P, wave, lane, part);
+      readcopy_dot(RCR, g.read_copy, x, lane, part);
     else
       frag_dot(F, x, lane, part);
-    write_rows<RBW>(part, lds[L.gam], lds, L, lds + L.coef, nrec, P, yout, wave, lane);
-    append_record<KIND, N>(a, b, hh, gq, (int)(nc % g.C), rs.a_idx, rs.v_idx, rs.k_idx, t);
+    write_rows<RBW>(part, lds[L.gam], lds, L, dec, lds + L.coef, nrec, P, yout, wave, lane);
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, nrec - 1, 0, (int)(nc % g.C), t);
   }
   if (t == 0) {
     a.n_committed[tile] = nc + 1;
@@ -711,44 +905,30 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   const LdsLayout L = lds_layout(KIND, cap, T, P, N);
   const float *tileS = a.s + (int64_t)tile * P * N;
 
-  Frag<N, RBW> F;
-  frag_load(F, tileS, P, wave, lane);
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, T, T);
+  sp.ia0 = (int64_t)b * T * g.H + hh;
+  sp.ias = g.H;
+  sp.iv0 = ((int64_t)b * T * g.H + hh) * P;
+  sp.ivs = (int64_t)g.H * P;
+  sp.ik0 = ((int64_t)b * T * g.G + gq) * N;
+  sp.iks = (int64_t)g.G * N;
+  sp.iq0 = sp.ik0;
+  sp.iqs = sp.iks;
 
-  RecSrc rs;
-  rs.n_ring = hb;
-  rs.n_in = T;
-  rs.slot0 = (int)(nk % g.C);
-  rs.a_idx = (int64_t)b * T * g.H + hh;
-  rs.a_str = g.H;
-  rs.v_idx = ((int64_t)b * T * g.H + hh) * P;
-  rs.v_str = (int64_t)g.H * P;
-  rs.k_idx = ((int64_t)b * T * g.G + gq) * N;
-  rs.k_str = (int64_t)g.G * N;
-  stage_records<KIND, N>(a, L, lds, b, hh, gq, rs, t);
-  for (int e = t; e < T * N; e += kThreads) {
-    const int tau = e / N, n = e - tau * N;
-    lds[L.q + e] = ld_in(a.q, rs.k_idx + tau * rs.k_str + n, g.bf16);
-  }
+  Frag<N, RBW> F;
+  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
 
   const float *xbase;
+  const float *dec = nullptr;
   if (KIND == RSSM_KIND_MAMBA2) {
-    // e[tau][j] = W[j, tau] (k_j . q_tau), W[j, tau] = prod_{j < m <= hb + tau} alpha_m for j <= hb + tau
-    const int g16 = t >> 4, l16 = t & 15;
-    const float *alpha = lds + L.alpha;
-    for (int d = g16; d < T * nrec; d += kThreads / 16) {
-      const int tau = d / nrec, j = d - tau * nrec;
-      const float *kr = lds + L.K + j * (N + 4);
-      const float *qr = lds + L.q + tau * N;
-      float acc = 0.f;
-#pragma unroll
-      for (int n = l16; n < N; n += 16) acc = fmaf(kr[n], qr[n], acc);
-      acc = sum16(acc);
-      if (l16 == 0) lds[L.coef + tau * cap + j] = (j <= hb + tau) ? suffix_decay(alpha, j, hb + tau) * acc : 0.f;
-    }
-    if (t < T) lds[L.gam + t] = suffix_decay(alpha, -1, hb + t);
+    // W[j, tau] = prod_{j < m <= hb + tau} alpha_m (dec rows), G_tau (gam), k_j . q_tau (coef rows)
+    for (int tau = wave; tau < T; tau += kWaves)
+      wave_decays(lds + L.alpha, hb + tau, lds + L.dec + tau * cap, lds + L.gam + tau, cap, lane);
+    kq_dots<N>(lds, L, cap, nrec, T, t);
     __syncthreads();
     xbase = lds + L.q;
+    dec = lds + L.dec;
   } else {
     gram_and_kq<N>(lds, L, cap, nrec, T, t);
     __syncthreads();
@@ -766,13 +946,11 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     float part[RBW];
     frag_dot(F, xbase + tau * N, lane, part);
     float *orow = a.out + (((int64_t)b * T + tau) * g.H + hh) * P;
-    write_rows<RBW>(part, lds[L.gam + tau], lds, L, lds + L.coef + tau * cap, hb + tau + 1, P, orow, wave, lane);
+    write_rows<RBW>(part, lds[L.gam + tau], lds, L, dec ? dec + tau * cap : nullptr, lds + L.coef + tau * cap,
+                    hb + tau + 1, P, orow, wave, lane);
   }
-  for (int tau = 0; tau < T; ++tau) {
-    int slot = (int)((nc + tau) % g.C);
-    append_record<KIND, N>(a, b, hh, gq, slot, rs.a_idx + tau * rs.a_str, rs.v_idx + tau * rs.v_str,
-                           rs.k_idx + tau * rs.k_str, t);
-  }
+  for (int tau = 0; tau < T; ++tau)
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, (int)((nc + tau) % g.C), t);
 }
 
 template <int KIND, int N, int RBW>
@@ -796,25 +974,20 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   const LdsLayout L = lds_layout(KIND, cap, 1, P, N);
   float *tileS = a.s + (int64_t)tile * P * N;
 
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, nrec, 0, 0);
   Frag<N, RBW> F;
-  frag_load(F, tileS, P, wave, lane);
-  RecSrc rs;
-  rs.n_ring = nrec;
-  rs.n_in = 0;
-  rs.slot0 = (int)(nk % g.C);
-  rs.a_idx = rs.a_str = rs.v_idx = rs.v_str = rs.k_idx = rs.k_str = 0;
-  stage_records<KIND, N>(a, L, lds, b, hh, gq, rs, t);
+  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
   if (KIND == RSSM_KIND_MAMBA2) {
-    for (int j = t; j < nrec; j += kThreads) lds[L.dec + j] = suffix_decay(lds + L.alpha, j, nrec - 1);
-    if (t == 0) lds[L.gam] = suffix_decay(lds + L.alpha, -1, nrec - 1);
+    if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
     __syncthreads();
     fold_m2(F, lds, L, nrec, P, wave, lane);
   } else {
     fold_gdn(F, lds, L, nrec, P, wave, lane);
   }
   frag_store(F, tileS, P, wave, lane);
-  if (g.read_copy != RSSM_READ_NONE) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+  if (g.read_copy != RSSM_READ_NONE)
+    frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
   if (t == 0) a.n_ckpt[tile] = nc;
 }
 
@@ -828,46 +1001,51 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   const int P = g.P;
   const LdsLayout L = lds_layout(KIND, 1, 1, P, N);
   float *tileS = a.s + (int64_t)tile * P * N;
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, 0, 0, 1, 1);
+  sp.slot0 = 0;
+  sp.ia0 = (int64_t)b * g.H + hh;
+  sp.iv0 = ((int64_t)b * g.H + hh) * P;
+  sp.ik0 = ((int64_t)b * g.G + gq) * N;
+  sp.iq0 = sp.ik0;
   Frag<N, RBW> F;
-  frag_load(F, tileS, P, wave, lane);
-  RecSrc rs;
-  rs.n_ring = 0;
-  rs.n_in = 1;
-  rs.slot0 = 0;
-  rs.a_idx = (int64_t)b * g.H + hh;
-  rs.a_str = 0;
-  rs.v_idx = ((int64_t)b * g.H + hh) * P;
-  rs.v_str = 0;
-  rs.k_idx = ((int64_t)b * g.G + gq) * N;
-  rs.k_str = 0;
-  stage_records<KIND, N>(a, L, lds, b, hh, gq, rs, t);
-  for (int n = t; n < N; n += kThreads) lds[L.q + n] = ld_in(a.q, rs.k_idx + n, g.bf16);
+  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
   const int c = (lane >> 4) * 4;
   const float al = lds[L.alpha];
-  float4 kf[N / 16];
+  const float *kr = lds + L.K + c;
+  float u[RBW];
+  if (KIND == RSSM_KIND_MAMBA2) {
 #pragma unroll
-  for (int f = 0; f < N / 16; ++f) kf[f] = *(const float4 *)(lds + L.K + c + 16 * f);
-#pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    const int row = frag_row(wave, lane, i);
-    const float vr = (row < P) ? lds[L.V + row] : 0.f;
-    float u;
-    if (KIND == RSSM_KIND_MAMBA2) {
-      u = vr;
-    } else {
-      float w = 0.f;
-#pragma unroll
-      for (int f = 0; f < N / 16; ++f) w = dot4(F.s[i][f], kf[f], w);
-      w = quad_sum(w);
-      u = lds[L.beta] * (vr - al * w);
+    for (int i = 0; i < RBW; ++i) {
+      const int row = frag_row(wave, lane, i);
+      u[i] = (row < P) ? lds[L.V + row] : 0.f;
     }
+  } else {
+    float w[RBW];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) w[i] = 0.f;
 #pragma unroll
     for (int f = 0; f < N / 16; ++f) {
-      F.s[i][f].x = fmaf(al, F.s[i][f].x, u * kf[f].x);
-      F.s[i][f].y = fmaf(al, F.s[i][f].y, u * kf[f].y);
-      F.s[i][f].z = fmaf(al, F.s[i][f].z, u * kf[f].z);
-      F.s[i][f].w = fmaf(al, F.s[i][f].w, u * kf[f].w);
+      const float4 kf = *(const float4 *)(kr + 16 * f);
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      const int row = frag_row(wave, lane, i);
+      const float vr = (row < P) ? lds[L.V + row] : 0.f;
+      u[i] = lds[L.beta] * (vr - al * quad_sum(w[i]));
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < N / 16; ++f) {
+    const float4 kf = *(const float4 *)(kr + 16 * f);
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
+      F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
+      F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
+      F.s[i][f].w = fmaf(al, F.s[i][f].w, u[i] * kf.w);
     }
   }
   frag_store(F, tileS, P, wave, lane);
@@ -894,7 +1072,8 @@ __global__ __launch_bounds__(kThreads) void k_init(Args a) {
   else
     frag_zero(F);
   frag_store(F, a.s + (int64_t)tile * P * N, P, wave, lane);
-  if (g.read_copy != RSSM_READ_NONE) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+  if (g.read_copy != RSSM_READ_NONE)
+    frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
   if (t == 0) {
     a.n_committed[tile] = 0;
     a.n_ckpt[tile] = 0;

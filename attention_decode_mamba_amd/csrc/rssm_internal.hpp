@@ -41,6 +41,7 @@ struct Args {
   const int32_t *n_accept;                 // commit
   int T;                                   // drafts (verify / commit)
   int min_records;                         // flush threshold
+  int vec16;                               // rows can be staged in 16-byte chunks
 };
 
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
@@ -55,7 +56,7 @@ __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P,
   int o = 0;
   l.alpha = o; o += up4(cap);
   l.beta = o;  o += up4(cap);
-  l.dec = o;   o += up4(cap);
+  l.dec = o;   o += up4(T * cap);
   l.coef = o;  o += up4(T * cap);
   l.cc = o;    o += up4(T * cap);
   l.gam = o;   o += up4(T);
