@@ -85,21 +85,20 @@ __device__ __forceinline__ void frag_zero(Frag<N, RBW> &F) {
     for (int f = 0; f < N / 16; ++f) F.s[i][f] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Rows past P (ragged tails) load a copy of row P - 1: every load is unconditional, so the
+// loads stay in flight across the staging code.  Such rows never interact with real rows
+// (all cross-lane sums stay within a row) and are never stored.
 template <int N, int RBW>
 __device__ __forceinline__ void frag_load(Frag<N, RBW> &F, const float *__restrict__ tile, int P, int wave,
                                           int lane) {
   const int c = (lane >> 4) * 4;
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
-    const int row = frag_row(wave, lane, i);
-    if (row < P) {
-      const float4 *src = (const float4 *)(tile + (int64_t)row * N + c);
+    int row = frag_row(wave, lane, i);
+    row = row < P ? row : P - 1;
+    const float4 *src = (const float4 *)(tile + (int64_t)row * N + c);
 #pragma unroll
-      for (int f = 0; f < N / 16; ++f) F.s[i][f] = src[4 * f];
-    } else {
-#pragma unroll
-      for (int f = 0; f < N / 16; ++f) F.s[i][f] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int f = 0; f < N / 16; ++f) F.s[i][f] = src[4 * f];
   }
 }
 
@@ -248,21 +247,22 @@ __device__ __forceinline__ void readcopy_load(RCopy<N, RBW> &R, int fmt, const u
   const int rowbytes = fmt == RSSM_READ_FP8 ? N : N / 2;
 #pragma unroll
   for (int i = 0; i < RBW; ++i) {
-    const int row = frag_row(wave, lane, i);
+    int row = frag_row(wave, lane, i);
+    row = row < P ? row : P - 1;                 // ragged rows: a copy of row P - 1, never stored
     const int64_t rowi = tile * P + row;
 #pragma unroll
     for (int ci = 0; ci < RCopy<N, RBW>::CI; ++ci) {
       const int ch = s + 4 * ci;
-      if (row < P && ch < nch) {
-        R.raw[i][ci] = *(const uint4 *)(codes + rowi * rowbytes + 16 * ch);
-        if (fmt == RSSM_READ_FP8)
-          R.sc[i][ci] = ((const float *)scales)[rowi * (N / 32) + ch / 2];
-        else
-          R.sc[i][ci] = __uint_as_float((uint32_t)scales[rowi * (N / 32) + ch] << 23);   // 2^(e8m0 - 127)
-      } else {
-        R.raw[i][ci] = make_uint4(0, 0, 0, 0);
-        R.sc[i][ci] = 0.f;
+      const int chc = ch < nch ? ch : nch - 1;
+      uint4 w = *(const uint4 *)(codes + rowi * rowbytes + 16 * chc);
+      float sc = fmt == RSSM_READ_FP8 ? ((const float *)scales)[rowi * (N / 32) + chc / 2]
+                                      : __uint_as_float((uint32_t)scales[rowi * (N / 32) + chc] << 23);
+      if (ch >= nch) {                           // no such chunk in this row: contributes nothing
+        w = make_uint4(0, 0, 0, 0);
+        sc = 0.f;
       }
+      R.raw[i][ci] = w;
+      R.sc[i][ci] = sc;
     }
   }
 }
@@ -355,56 +355,56 @@ __device__ __forceinline__ int stage_chunks(const StageSpec &sp, int epc) {
   return sp.nrec * (sp.P / epc) + sp.nrec * (sp.N / epc) + sp.nq * (sp.N / epc);
 }
 
-template <int U>
+// Issue one round of staging loads.  Every lane issues every load (idle chunks re-read the
+// last valid chunk and are marked dst = -1), so the loads form straight-line code.
+template <int U, bool BF, bool HASB>
 __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R, int base, float *lds, int t,
                                             bool with_scalars) {
-  const int es = sp.bf16 ? 2 : 4;
-  const int epc = 16 / es;
+  constexpr int es = BF ? 2 : 4;
+  constexpr int epc = 16 / es;
   const int cpv = sp.P / epc, cpk = sp.N / epc;
   const int nV = sp.nrec * cpv, nK = sp.nrec * cpk, total = nV + nK + sp.nq * cpk;
   if (with_scalars) {
-    R.a = 0.f;
-    R.b = 0.f;
-    if (t < sp.nrec) {
-      if (t < sp.n_ring) {
-        const int64_t i = sp.hrow + ring_slot(sp, t);
-        R.a = ld_in(sp.rA, i, sp.bf16);
-        if (sp.rB) R.b = ld_in(sp.rB, i, sp.bf16);
-      } else {
-        const int64_t i = sp.ia0 + (int64_t)(t - sp.n_ring) * sp.ias;
-        R.a = ld_in(sp.iA, i, sp.bf16);
-        if (sp.iB) R.b = ld_in(sp.iB, i, sp.bf16);
-      }
+    const int j = t < sp.nrec ? t : sp.nrec - 1;
+    const bool ring = j < sp.n_ring;
+    const int64_t ri = sp.hrow + ring_slot(sp, j);
+    const int64_t ii = sp.ia0 + (int64_t)(j - sp.n_ring) * sp.ias;
+    const uint8_t *pa = ring ? sp.rA + ri * es : (const uint8_t *)sp.iA + ii * es;
+    R.a = BF ? bf16f(*(const uint16_t *)pa) : *(const float *)pa;
+    if (HASB) {
+      const uint8_t *pb = ring ? sp.rB + ri * es : (const uint8_t *)sp.iB + ii * es;
+      R.b = BF ? bf16f(*(const uint16_t *)pb) : *(const float *)pb;
+    } else {
+      R.b = 0.f;
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = base + u * kThreads + t;
-    R.dst[u] = -1;
-    R.raw[u] = make_uint4(0, 0, 0, 0);
-    if (c < total) {
-      const uint8_t *src;
-      if (c < nV) {
-        const int j = c / cpv, e = (c - j * cpv) * epc;
-        src = j < sp.n_ring ? sp.rV + ((sp.hrow + ring_slot(sp, j)) * sp.P + e) * es
-                            : (const uint8_t *)sp.iV + (sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + e) * es;
-        R.dst[u] = (int)(sp.V - lds) + j * sp.P + e;
-      } else if (c < nV + nK) {
-        const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
-        src = j < sp.n_ring ? sp.rK + ((sp.krow + ring_slot(sp, j)) * sp.N + e) * es
-                            : (const uint8_t *)sp.iK + (sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + e) * es;
-        R.dst[u] = (int)(sp.K - lds) + j * (sp.N + 4) + e;
-      } else {
-        const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
-        src = (const uint8_t *)sp.iQ + (sp.iq0 + (int64_t)r * sp.iqs + e) * es;
-        R.dst[u] = (int)(sp.Q - lds) + r * sp.N + e;
-      }
-      R.raw[u] = *(const uint4 *)src;
+    const int c0 = base + u * kThreads + t;
+    const int c = c0 < total ? c0 : total - 1;
+    const uint8_t *src;
+    int dst;
+    if (c < nV) {
+      const int j = c / cpv, e = (c - j * cpv) * epc;
+      src = j < sp.n_ring ? sp.rV + ((sp.hrow + ring_slot(sp, j)) * sp.P + e) * es
+                          : (const uint8_t *)sp.iV + (sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + e) * es;
+      dst = (int)(sp.V - lds) + j * sp.P + e;
+    } else if (c < nV + nK) {
+      const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
+      src = j < sp.n_ring ? sp.rK + ((sp.krow + ring_slot(sp, j)) * sp.N + e) * es
+                          : (const uint8_t *)sp.iK + (sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + e) * es;
+      dst = (int)(sp.K - lds) + j * (sp.N + 4) + e;
+    } else {
+      const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
+      src = (const uint8_t *)sp.iQ + (sp.iq0 + (int64_t)r * sp.iqs + e) * es;
+      dst = (int)(sp.Q - lds) + r * sp.N + e;
     }
+    R.raw[u] = *(const uint4 *)src;
+    R.dst[u] = c0 < total ? dst : -1;
   }
 }
 
-template <int U>
+template <int U, bool BF>
 __device__ __forceinline__ void stage_commit(const StageSpec &sp, const StageRegs<U> &R, float *lds, int t,
                                              bool with_scalars) {
   if (with_scalars && t < sp.nrec) {
@@ -416,7 +416,7 @@ __device__ __forceinline__ void stage_commit(const StageSpec &sp, const StageReg
     if (R.dst[u] < 0) continue;
     float *d = lds + R.dst[u];
     const uint4 w = R.raw[u];
-    if (sp.bf16) {
+    if (BF) {
       *(float4 *)d = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
                                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
       *(float4 *)(d + 4) = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
@@ -496,19 +496,27 @@ __device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L
 
 // Stage a tile's records with the checkpoint loads in flight: record loads are issued
 // first, then `issue_tile()` (the checkpoint or read-copy loads), then the LDS writes.
-template <int U, class IssueTile>
+template <int U, bool BF, bool HASB, class IssueTile>
+__device__ __forceinline__ void stage_vec_with_tile(const StageSpec &sp, float *lds, int t, IssueTile &&issue_tile) {
+  StageRegs<U> SR;
+  stage_issue<U, BF, HASB>(sp, SR, 0, lds, t, true);
+  issue_tile();
+  stage_commit<U, BF>(sp, SR, lds, t, true);
+  const int total = stage_chunks(sp, BF ? 8 : 4);
+  for (int base = kThreads * U; base < total; base += kThreads * U) {
+    stage_issue<U, BF, HASB>(sp, SR, base, lds, t, false);
+    stage_commit<U, BF>(sp, SR, lds, t, false);
+  }
+}
+
+template <int U, bool HASB, class IssueTile>
 __device__ __forceinline__ void stage_with_tile(const Args &a, const StageSpec &sp, float *lds, int t,
                                                 IssueTile &&issue_tile) {
   if (a.vec16) {
-    StageRegs<U> SR;
-    stage_issue(sp, SR, 0, lds, t, true);
-    issue_tile();
-    stage_commit(sp, SR, lds, t, true);
-    const int total = stage_chunks(sp, sp.bf16 ? 8 : 4);
-    for (int base = kThreads * U; base < total; base += kThreads * U) {
-      stage_issue(sp, SR, base, lds, t, false);
-      stage_commit(sp, SR, lds, t, false);
-    }
+    if (sp.bf16)
+      stage_vec_with_tile<U, true, HASB>(sp, lds, t, issue_tile);
+    else
+      stage_vec_with_tile<U, false, HASB>(sp, lds, t, issue_tile);
   } else {
     issue_tile();
     stage_scalar(sp, t);
@@ -821,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
 
   Frag<N, RBW> F;
   RCopy<N, RBW> RCR;
-  stage_with_tile<U>(a, sp, lds, t, [&]() {
+  stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
     if (from_copy)
       readcopy_load(RCR, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
     else
@@ -916,7 +924,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   sp.iqs = sp.iks;
 
   Frag<N, RBW> F;
-  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
 
   const float *xbase;
@@ -976,7 +984,7 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, nrec, 0, 0);
   Frag<N, RBW> F;
-  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
   if (KIND == RSSM_KIND_MAMBA2) {
     if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
@@ -1008,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   sp.ik0 = ((int64_t)b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
   Frag<N, RBW> F;
-  stage_with_tile<4>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
   __syncthreads();
   const int c = (lane >> 4) * 4;
   const float al = lds[L.alpha];

@@ -308,7 +308,7 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps):
         wb = sum(w) / len(w) * 1024.0 * fw
         res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
-                      "write_kib_per_dispatch": w}
+                      "write_mib_per_dispatch_min_max": [min(w) / 1024.0 * fw, max(w) / 1024.0 * fw]}
     W = 16
     hs = [((W + i) % wl.L) + 1 for i in range(steps)]
     alg = sum(step_bytes(wl, h)["total"] for h in hs) / steps
@@ -337,7 +337,7 @@ def main():
     if args.summarize_counters:
         r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], PROFILE_SUMMARY,
                                args.counter_command, args.batch or 256, args.steps)
-        print(json.dumps({k: v for k, v in r.items() if k != "replay_decode"}, indent=1))
+        print(json.dumps(r, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the decode path shards over "
