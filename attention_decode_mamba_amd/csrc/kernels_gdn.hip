@@ -17,7 +17,7 @@ hipError_t launch_decode_gdn(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_decode<kKind, n, r, true>), grid_of(a), dim3(kThreads), lds, s, a);  \
     return hipGetLastError();                                                                  \
   }
-    RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+    RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
   }
 #define CALL(n, r)                                                                             \
@@ -25,7 +25,7 @@ hipError_t launch_decode_gdn(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_decode<kKind, n, r, false>), grid_of(a), dim3(kThreads), lds, s, a); \
     return hipGetLastError();                                                                  \
   }
-  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 
@@ -36,7 +36,7 @@ hipError_t launch_verify_gdn(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_verify<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);     \
     return hipGetLastError();                                                               \
   }
-  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 
@@ -47,7 +47,7 @@ hipError_t launch_flush_gdn(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_flush<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);      \
     return hipGetLastError();                                                               \
   }
-  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 
@@ -58,7 +58,7 @@ hipError_t launch_conventional_gdn(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_conventional<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a); \
     return hipGetLastError();                                                               \
   }
-  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 

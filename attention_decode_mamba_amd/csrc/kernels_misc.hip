@@ -40,7 +40,7 @@ hipError_t launch_init(const Args &a, hipStream_t s) {
     hipLaunchKernelGGL((k_init<n, r>), grid, dim3(kThreads), 0, s, a);       \
     return hipGetLastError();                                                \
   }
-  RSSM_DISPATCH(a.g.N, rbw_for(a.g.P), CALL)
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 

@@ -3,12 +3,12 @@
 // One workgroup (4 waves of 64 lanes) owns one (sequence, value-head) tile: the
 // P x N fp32 checkpoint tile S_ckpt, its ring records and its cursor replica.
 //
-// Register layout of a tile ("fragment layout"): the tile is cut into 16x16
-// fragments; row block rb = wave + 4*i (i < RBW) belongs to one wave, and lane l
-// holds, for every fragment f along N, the float4 S[rb*16 + l%16][16f + 4(l/16) .. +3].
-// A row's N values are thus spread over 4 lanes (l/16 = 0..3) times N/16 registers,
-// so a row dot product is N/16 float4 FMAs per lane plus two cross-lane adds; and
-// the layout is the operand/accumulator layout of the 16x16x4 fp32 MFMA.
+// Register layout of a tile ("row-octet layout"): row group g = wave + 4*i (i < RGW)
+// holds rows 8g .. 8g+7; lane l takes row 8g + l/8 and, for every 32-column fragment f,
+// the float4 S[8g + l/8][32f + 4(l%8) .. +3].  One load instruction therefore covers
+// 8 rows x 128 contiguous bytes; a row dot product is N/32 float4 FMAs per lane plus
+// three cross-lane adds within the 8 lanes of the row; and a 32-element read-copy block
+// is exactly one fragment of one row.
 //
 // Latency structure of every kernel: the cursor is read first; then all loads of
 // the ring records, step inputs and queries are issued (16-byte chunks), then the
@@ -39,15 +39,18 @@ __device__ __forceinline__ int tile_of_block(int ntiles) {
   return bid;
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
+// Sum / max over the 8 lanes that share a row (lanes differing in bits 0..2).
+__device__ __forceinline__ float oct_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
   return v;
 }
 
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
+__device__ __forceinline__ float oct_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
   return v;
 }
 
@@ -70,49 +73,62 @@ __device__ __forceinline__ float wave_suffix_product(float x, int lane) {
 }
 
 // ---------------------------------------------------------------- fragments
-template <int N, int RBW>
+template <int N, int RGW>
 struct Frag {
-  float4 s[RBW][N / 16];
+  float4 s[RGW][N / 32];
 };
 
-__device__ __forceinline__ int frag_row(int wave, int lane, int i) { return (wave + kWaves * i) * 16 + (lane & 15); }
+__device__ __forceinline__ int frag_row(int wave, int lane, int i) { return 8 * (wave + kWaves * i) + (lane >> 3); }
+__device__ __forceinline__ int frag_col(int lane) { return 4 * (lane & 7); }
 
-template <int N, int RBW>
-__device__ __forceinline__ void frag_zero(Frag<N, RBW> &F) {
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ float4 ld4(const float4 *p) {
+  if (NT) {
+    const f4v v = __builtin_nontemporal_load((const f4v *)p);
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+  return *p;
+}
+
+template <int N, int RGW>
+__device__ __forceinline__ void frag_zero(Frag<N, RGW> &F) {
 #pragma unroll
-  for (int i = 0; i < RBW; ++i)
+  for (int i = 0; i < RGW; ++i)
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) F.s[i][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int f = 0; f < N / 32; ++f) F.s[i][f] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // Rows past P (ragged tails) load a copy of row P - 1: every load is unconditional, so the
 // loads stay in flight across the staging code.  Such rows never interact with real rows
-// (all cross-lane sums stay within a row) and are never stored.
-template <int N, int RBW>
-__device__ __forceinline__ void frag_load(Frag<N, RBW> &F, const float *__restrict__ tile, int P, int wave,
+// (all cross-lane sums stay within a row) and are never stored.  NT: streaming loads
+// (the tile is read once per step).
+template <int N, int RGW, bool NT>
+__device__ __forceinline__ void frag_load(Frag<N, RGW> &F, const float *__restrict__ tile, int P, int wave,
                                           int lane) {
-  const int c = (lane >> 4) * 4;
+  const int c = frag_col(lane);
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     int row = frag_row(wave, lane, i);
     row = row < P ? row : P - 1;
     const float4 *src = (const float4 *)(tile + (int64_t)row * N + c);
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) F.s[i][f] = src[4 * f];
+    for (int f = 0; f < N / 32; ++f) F.s[i][f] = ld4<NT>(src + 8 * f);
   }
 }
 
-template <int N, int RBW>
-__device__ __forceinline__ void frag_store(const Frag<N, RBW> &F, float *__restrict__ tile, int P, int wave,
+template <int N, int RGW>
+__device__ __forceinline__ void frag_store(const Frag<N, RGW> &F, float *__restrict__ tile, int P, int wave,
                                            int lane) {
-  const int c = (lane >> 4) * 4;
+  const int c = frag_col(lane);
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     const int row = frag_row(wave, lane, i);
     if (row < P) {
       float4 *dst = (float4 *)(tile + (int64_t)row * N + c);
 #pragma unroll
-      for (int f = 0; f < N / 16; ++f) dst[4 * f] = F.s[i][f];
+      for (int f = 0; f < N / 32; ++f) dst[8 * f] = F.s[i][f];
     }
   }
 }
@@ -126,16 +142,28 @@ __device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc)
 }
 
 // Per-lane partial of S x for the lane's rows (x: N floats in LDS).
-template <int N, int RBW>
-__device__ __forceinline__ void frag_dot(const Frag<N, RBW> &F, const float *x, int lane, float (&out)[RBW]) {
-  const int c = (lane >> 4) * 4;
+template <int N, int RGW>
+__device__ __forceinline__ void frag_dot(const Frag<N, RGW> &F, const float *x, int lane, float (&out)[RGW]) {
+  const int c = frag_col(lane);
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) out[i] = 0.f;
+  for (int i = 0; i < RGW; ++i) out[i] = 0.f;
 #pragma unroll
-  for (int f = 0; f < N / 16; ++f) {
-    const float4 xv = *(const float4 *)(x + 16 * f + c);
+  for (int f = 0; f < N / 32; ++f) {
+    const float4 xv = *(const float4 *)(x + 32 * f + c);
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) out[i] = dot4(F.s[i][f], xv, out[i]);
+    for (int i = 0; i < RGW; ++i) out[i] = dot4(F.s[i][f], xv, out[i]);
+  }
+}
+
+// Row results of a per-lane partial: lanes with l%8 == 0 write out[row].
+template <int RGW>
+__device__ __forceinline__ void write_row_sums(const float (&part)[RGW], int P, float *__restrict__ out, int wave,
+                                               int lane) {
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) {
+    const int row = frag_row(wave, lane, i);
+    const float y = oct_sum(part[i]);
+    if ((lane & 7) == 0 && row < P) out[row] = y;
   }
 }
 
@@ -176,50 +204,40 @@ __device__ __forceinline__ int ilog2f(float a) {
 }
 
 // Quantise the tile held in registers and store the read copy (fp8 or MXFP4).
-// Blocks are 32 consecutive columns: fragments 2m and 2m+1 across the 4 lanes of a row.
-template <int N, int RBW>
-__device__ void frag_store_read_copy(const Frag<N, RBW> &F, int fmt, uint8_t *__restrict__ codes,
+// A 32-element block is fragment f of one row: 8 lanes x 4 values.
+template <int N, int RGW>
+__device__ void frag_store_read_copy(const Frag<N, RGW> &F, int fmt, uint8_t *__restrict__ codes,
                                      uint8_t *__restrict__ scales, int64_t tile, int P, int wave, int lane) {
-  const int c = (lane >> 4) * 4;
-  const bool lead = (lane >> 4) == 0;
+  const int c = frag_col(lane);
+  const bool lead = (lane & 7) == 0;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     const int row = frag_row(wave, lane, i);
     const int64_t rowi = tile * P + row;
 #pragma unroll
-    for (int m = 0; m < N / 32; ++m) {
-      const float4 v0 = F.s[i][2 * m], v1 = F.s[i][2 * m + 1];
-      float am = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-      am = quad_max(am);
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 v = F.s[i][f];
+      float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+      am = oct_max(am);
       if (fmt == RSSM_READ_FP8) {
         const float sc = __fdiv_rn(am, 448.0f);
-        uint32_t w0 = 0, w1 = 0;
-        if (sc > 0.f) {
-          w0 = f32_to_e4m3(__fdiv_rn(v0.x, sc)) | (f32_to_e4m3(__fdiv_rn(v0.y, sc)) << 8) |
-               (f32_to_e4m3(__fdiv_rn(v0.z, sc)) << 16) | (f32_to_e4m3(__fdiv_rn(v0.w, sc)) << 24);
-          w1 = f32_to_e4m3(__fdiv_rn(v1.x, sc)) | (f32_to_e4m3(__fdiv_rn(v1.y, sc)) << 8) |
-               (f32_to_e4m3(__fdiv_rn(v1.z, sc)) << 16) | (f32_to_e4m3(__fdiv_rn(v1.w, sc)) << 24);
-        }
+        uint32_t w = 0;
+        if (sc > 0.f)
+          w = f32_to_e4m3(__fdiv_rn(v.x, sc)) | (f32_to_e4m3(__fdiv_rn(v.y, sc)) << 8) |
+              (f32_to_e4m3(__fdiv_rn(v.z, sc)) << 16) | (f32_to_e4m3(__fdiv_rn(v.w, sc)) << 24);
         if (row < P) {
-          uint8_t *dst = codes + rowi * N;
-          *(uint32_t *)(dst + 32 * m + c) = w0;
-          *(uint32_t *)(dst + 32 * m + 16 + c) = w1;
-          if (lead) ((float *)scales)[rowi * (N / 32) + m] = sc;
+          *(uint32_t *)(codes + rowi * N + 32 * f + c) = w;
+          if (lead) ((float *)scales)[rowi * (N / 32) + f] = sc;
         }
       } else {
         int E = (am > 0.f) ? ilog2f(am) - 2 : -126;
         E = E < -126 ? -126 : (E > 127 ? 127 : E);                        // scale stays a normal float
         const float inv = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E (E <= 125 for finite amax)
-        const uint32_t h0 = f32_to_e2m1(v0.x * inv) | (f32_to_e2m1(v0.y * inv) << 4) |
-                            (f32_to_e2m1(v0.z * inv) << 8) | (f32_to_e2m1(v0.w * inv) << 12);
-        const uint32_t h1 = f32_to_e2m1(v1.x * inv) | (f32_to_e2m1(v1.y * inv) << 4) |
-                            (f32_to_e2m1(v1.z * inv) << 8) | (f32_to_e2m1(v1.w * inv) << 12);
+        const uint32_t h = f32_to_e2m1(v.x * inv) | (f32_to_e2m1(v.y * inv) << 4) |
+                           (f32_to_e2m1(v.z * inv) << 8) | (f32_to_e2m1(v.w * inv) << 12);
         if (row < P) {
-          uint8_t *dst = codes + rowi * (N / 2);
-          *(uint16_t *)(dst + 16 * m + c / 2) = (uint16_t)h0;
-          *(uint16_t *)(dst + 16 * m + 8 + c / 2) = (uint16_t)h1;
-          if (lead) scales[rowi * (N / 32) + m] = (uint8_t)(E + 127);
+          *(uint16_t *)(codes + rowi * (N / 2) + 16 * f + c / 2) = (uint16_t)h;
+          if (lead) scales[rowi * (N / 32) + f] = (uint8_t)(E + 127);
         }
       }
     }
@@ -228,36 +246,45 @@ __device__ void frag_store_read_copy(const Frag<N, RBW> &F, int fmt, uint8_t *__
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-// Read-copy registers of the lane's rows: fp8 lanes take 16-byte chunks (16 codes)
-// ch = l/16 + 4*ci of a row; MXFP4 lanes take 16-byte chunks of 32 codes (one block).
-template <int N, int RBW>
+// Read-copy registers of the lane's rows.  A row's codes are cut into chunks of 16
+// elements (fp8: 16 bytes, MXFP4: 8 bytes); lane l takes chunks k = l%8 + 8*ci, so one
+// load instruction covers 8 rows x 128 (fp8) or 64 (MXFP4) contiguous bytes.
+template <int N, int RGW>
 struct RCopy {
-  static constexpr int NCH = N / 16;            // fp8 chunks per row (MXFP4 uses N / 32)
-  static constexpr int CI = (NCH + 3) / 4;
-  uint4 raw[RBW][CI];
-  float sc[RBW][CI];
+  static constexpr int NCH = N / 16;
+  static constexpr int CI = (NCH + 7) / 8;
+  uint4 raw[RGW][CI];
+  float sc[RGW][CI];
 };
 
-template <int N, int RBW>
-__device__ __forceinline__ void readcopy_load(RCopy<N, RBW> &R, int fmt, const uint8_t *__restrict__ codes,
+template <int N, int RGW>
+__device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const uint8_t *__restrict__ codes,
                                               const uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
                                               int lane) {
-  const int s = lane >> 4;
-  const int nch = fmt == RSSM_READ_FP8 ? N / 16 : N / 32;
-  const int rowbytes = fmt == RSSM_READ_FP8 ? N : N / 2;
+  constexpr int NCH = RCopy<N, RGW>::NCH;
+  const int c8 = lane & 7;
+  const bool fp8 = fmt == RSSM_READ_FP8;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     int row = frag_row(wave, lane, i);
     row = row < P ? row : P - 1;                 // ragged rows: a copy of row P - 1, never stored
     const int64_t rowi = tile * P + row;
 #pragma unroll
-    for (int ci = 0; ci < RCopy<N, RBW>::CI; ++ci) {
-      const int ch = s + 4 * ci;
-      const int chc = ch < nch ? ch : nch - 1;
-      uint4 w = *(const uint4 *)(codes + rowi * rowbytes + 16 * chc);
-      float sc = fmt == RSSM_READ_FP8 ? ((const float *)scales)[rowi * (N / 32) + chc / 2]
-                                      : __uint_as_float((uint32_t)scales[rowi * (N / 32) + chc] << 23);
-      if (ch >= nch) {                           // no such chunk in this row: contributes nothing
+    for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
+      const int k = c8 + 8 * ci;
+      const int kc = k < NCH ? k : NCH - 1;
+      uint4 w;
+      float sc;
+      if (fp8) {
+        const f4v v = __builtin_nontemporal_load((const f4v *)(codes + rowi * N + 16 * kc));
+        w = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+        sc = ((const float *)scales)[rowi * (N / 32) + kc / 2];
+      } else {
+        const uint2 v = *(const uint2 *)(codes + rowi * (N / 2) + 8 * kc);
+        w = make_uint4(v.x, v.y, 0, 0);
+        sc = __uint_as_float((uint32_t)scales[rowi * (N / 32) + kc / 2] << 23);   // 2^(e8m0 - 127)
+      }
+      if (k >= NCH) {                             // no such chunk in this row: contributes nothing
         w = make_uint4(0, 0, 0, 0);
         sc = 0.f;
       }
@@ -268,54 +295,51 @@ __device__ __forceinline__ void readcopy_load(RCopy<N, RBW> &R, int fmt, const u
 }
 
 // Per-lane partial of S_read x from loaded read-copy registers.
-template <int N, int RBW>
-__device__ __forceinline__ void readcopy_dot(const RCopy<N, RBW> &R, int fmt, const float *x, int lane,
-                                             float (&out)[RBW]) {
-  const int s = lane >> 4;
+template <int N, int RGW>
+__device__ __forceinline__ void readcopy_dot(const RCopy<N, RGW> &R, int fmt, const float *x, int lane,
+                                             float (&out)[RGW]) {
+  const int c8 = lane & 7;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     float acc = 0.f;
 #pragma unroll
-    for (int ci = 0; ci < RCopy<N, RBW>::CI; ++ci) {
-      const int ch = s + 4 * ci;
-      const uint32_t w[4] = {R.raw[i][ci].x, R.raw[i][ci].y, R.raw[i][ci].z, R.raw[i][ci].w};
+    for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
+      const int k = c8 + 8 * ci;
+      const float *xp = x + 16 * (k < RCopy<N, RGW>::NCH ? k : 0);
+      const uint4 w = R.raw[i][ci];
+      const float sc = R.sc[i][ci];
       if (fmt == RSSM_READ_FP8) {
-        if (ch < N / 16) {
-          const float *xp = x + 16 * ch;
-          float d = 0.f;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        float d = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[q], 1.0f, false);
-            const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[q], 1.0f, true);
-            const float4 xv = *(const float4 *)(xp + 4 * q);
-            d = fmaf(lo[0], xv.x, d);
-            d = fmaf(lo[1], xv.y, d);
-            d = fmaf(hi[0], xv.z, d);
-            d = fmaf(hi[1], xv.w, d);
-          }
-          acc = fmaf(R.sc[i][ci], d, acc);
+        for (int q = 0; q < 4; ++q) {
+          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws[q], 1.0f, false);
+          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws[q], 1.0f, true);
+          const float4 xv = *(const float4 *)(xp + 4 * q);
+          d = fmaf(lo[0], xv.x, d);
+          d = fmaf(lo[1], xv.y, d);
+          d = fmaf(hi[0], xv.z, d);
+          d = fmaf(hi[1], xv.w, d);
         }
+        acc = fmaf(sc, d, acc);
       } else {
-        if (ch < N / 32) {
-          const float *xp = x + 32 * ch;
-          const float sc = R.sc[i][ci];
+        const uint32_t ws[2] = {w.x, w.y};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 xa = *(const float4 *)(xp + 8 * q);
-            const float4 xb = *(const float4 *)(xp + 8 * q + 4);
-            const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 0);
-            const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 1);
-            const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 2);
-            const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], sc, 3);
-            acc = fmaf(v0[0], xa.x, acc);
-            acc = fmaf(v0[1], xa.y, acc);
-            acc = fmaf(v1[0], xa.z, acc);
-            acc = fmaf(v1[1], xa.w, acc);
-            acc = fmaf(v2[0], xb.x, acc);
-            acc = fmaf(v2[1], xb.y, acc);
-            acc = fmaf(v3[0], xb.z, acc);
-            acc = fmaf(v3[1], xb.w, acc);
-          }
+        for (int q = 0; q < 2; ++q) {
+          const float4 xa = *(const float4 *)(xp + 8 * q);
+          const float4 xb = *(const float4 *)(xp + 8 * q + 4);
+          const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 0);
+          const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 1);
+          const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 2);
+          const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 3);
+          acc = fmaf(v0[0], xa.x, acc);
+          acc = fmaf(v0[1], xa.y, acc);
+          acc = fmaf(v1[0], xa.z, acc);
+          acc = fmaf(v1[1], xa.w, acc);
+          acc = fmaf(v2[0], xb.x, acc);
+          acc = fmaf(v2[1], xb.y, acc);
+          acc = fmaf(v3[0], xb.z, acc);
+          acc = fmaf(v3[1], xb.w, acc);
         }
       }
     }
@@ -696,15 +720,15 @@ __device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int
 
 // ---------------------------------------------------------------- folds
 // Mamba-2 fold: S <- G S + sum_j d_j v_j k_j^T (decays in L.dec, G in L.gam).
-template <int N, int RBW>
-__device__ void fold_m2(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
+template <int N, int RGW>
+__device__ void fold_m2(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
                         int lane) {
-  const int c = (lane >> 4) * 4;
+  const int c = frag_col(lane);
   const float G = lds[L.gam];
 #pragma unroll
-  for (int i = 0; i < RBW; ++i)
+  for (int i = 0; i < RGW; ++i)
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) {
+    for (int f = 0; f < N / 32; ++f) {
       F.s[i][f].x *= G;
       F.s[i][f].y *= G;
       F.s[i][f].z *= G;
@@ -713,17 +737,17 @@ __device__ void fold_m2(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, i
   for (int j = 0; j < nrec; ++j) {
     const float dj = lds[L.dec + j];
     const float *kr = lds + L.K + j * (N + 4) + c;
-    float vr[RBW];
+    float vr[RGW];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < RGW; ++i) {
       const int row = frag_row(wave, lane, i);
       vr[i] = (row < P) ? lds[L.V + j * P + row] * dj : 0.f;
     }
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) {
-      const float4 kf = *(const float4 *)(kr + 16 * f);
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) {
+      for (int i = 0; i < RGW; ++i) {
         F.s[i][f].x = fmaf(vr[i], kf.x, F.s[i][f].x);
         F.s[i][f].y = fmaf(vr[i], kf.y, F.s[i][f].y);
         F.s[i][f].z = fmaf(vr[i], kf.z, F.s[i][f].z);
@@ -735,35 +759,35 @@ __device__ void fold_m2(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, i
 
 // Gated DeltaNet fold, one delta-rule update per record in registers:
 // S <- a S ; u = b (v - S k) ; S <- S + u k^T.
-template <int N, int RBW>
-__device__ void fold_gdn(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
+template <int N, int RGW>
+__device__ void fold_gdn(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
                          int lane) {
-  const int c = (lane >> 4) * 4;
+  const int c = frag_col(lane);
   for (int j = 0; j < nrec; ++j) {
     const float al = lds[L.alpha + j], be = lds[L.beta + j];
     const float *kr = lds + L.K + j * (N + 4) + c;
-    float w[RBW];
+    float w[RGW];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) w[i] = 0.f;
+    for (int i = 0; i < RGW; ++i) w[i] = 0.f;
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) {
-      const float4 kf = *(const float4 *)(kr + 16 * f);
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
+      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
     }
-    float u[RBW];
+    float u[RGW];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      const float wi = quad_sum(w[i]);
+    for (int i = 0; i < RGW; ++i) {
+      const float wi = oct_sum(w[i]);
       const int row = frag_row(wave, lane, i);
       const float vr = (row < P) ? lds[L.V + j * P + row] : 0.f;
       u[i] = be * (vr - al * wi);
     }
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) {
-      const float4 kf = *(const float4 *)(kr + 16 * f);
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) {
+      for (int i = 0; i < RGW; ++i) {
         F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
         F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
         F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
@@ -775,23 +799,23 @@ __device__ void fold_gdn(Frag<N, RBW> &F, const float *lds, const LdsLayout &L, 
 
 // Output rows: y[row] = G * (S x)[row] + sum_{j < n} w_j v_j[row], where w_j = dec[j] * coef[j]
 // (Mamba-2: decay times k_j . q) or w_j = coef[j] (GDN: already d_j b_j c_j; dec == null).
-// Lanes with l/16 = s take records j = s mod 4.
-template <int RBW>
-__device__ __forceinline__ void write_rows(const float (&part)[RBW], float G, const float *lds, const LdsLayout &L,
+// The 8 lanes of a row take records j = l%8 mod 8.
+template <int RGW>
+__device__ __forceinline__ void write_rows(const float (&part)[RGW], float G, const float *lds, const LdsLayout &L,
                                            const float *dec, const float *coef, int n, int P,
                                            float *__restrict__ out, int wave, int lane) {
-  const int s = lane >> 4;
+  const int c8 = lane & 7;
 #pragma unroll
-  for (int i = 0; i < RBW; ++i) {
+  for (int i = 0; i < RGW; ++i) {
     const int row = frag_row(wave, lane, i);
     float buf = 0.f;
     if (row < P)
-      for (int j = s; j < n; j += 4) {
+      for (int j = c8; j < n; j += 8) {
         const float w = dec ? dec[j] * coef[j] : coef[j];
         buf = fmaf(w, lds[L.V + j * P + row], buf);
       }
-    const float y = quad_sum(fmaf(G, part[i], buf));
-    if (s == 0 && row < P) out[row] = y;
+    const float y = oct_sum(fmaf(G, part[i], buf));
+    if (c8 == 0 && row < P) out[row] = y;
   }
 }
 
@@ -799,9 +823,9 @@ __device__ __forceinline__ void write_rows(const float (&part)[RBW], float G, co
 
 // U: staging chunks per thread per round (2 covers a 17-record Mamba-2 window at 64 x 128
 // in bf16 in one round).  RC: the kernel serves non-fold steps from the read copy.
-template <int KIND, int N, int RBW, bool RC>
+template <int KIND, int N, int RGW, bool RC>
 __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
-  constexpr int U = (KIND == RSSM_KIND_GDN || RBW > 1) ? 4 : 2;
+  constexpr int U = (KIND == RSSM_KIND_GDN || RGW > 2) ? 4 : 2;
   extern __shared__ float lds[];
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
@@ -827,14 +851,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   sp.ik0 = ((int64_t)b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
 
-  Frag<N, RBW> F;
-  RCopy<N, RBW> RCR;
-  stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
-    if (from_copy)
+  Frag<N, RGW> F;
+  RCopy<N, RGW> RCR;
+  // the tile is streamed with nontemporal loads when it is only read (non-fold steps); a
+  // fold step writes it back, and keeps ordinary loads
+  if (from_copy)
+    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
       readcopy_load(RCR, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
-    else
-      frag_load(F, tileS, P, wave, lane);
-  });
+    });
+  else if (flush)
+    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
+  else
+    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
   __syncthreads();
 
   float *yout = a.out + ((int64_t)b * g.H + hh) * P;
@@ -848,14 +876,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     }
     frag_store(F, tileS, P, wave, lane);
     if (RC) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
-    float part[RBW];
+    float part[RGW];
     frag_dot(F, lds + L.q, lane, part);
-#pragma unroll
-    for (int i = 0; i < RBW; ++i) {
-      const int row = frag_row(wave, lane, i);
-      const float y = quad_sum(part[i]);
-      if ((lane >> 4) == 0 && row < P) yout[row] = y;
-    }
+    write_row_sums<RGW>(part, P, yout, wave, lane);
   } else {
     const float *x;
     const float *dec = nullptr;
@@ -874,12 +897,12 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       __syncthreads();
       x = lds + L.r;
     }
-    float part[RBW];
+    float part[RGW];
     if (from_copy)
       readcopy_dot(RCR, g.read_copy, x, lane, part);
     else
       frag_dot(F, x, lane, part);
-    write_rows<RBW>(part, lds[L.gam], lds, L, dec, lds + L.coef, nrec, P, yout, wave, lane);
+    write_rows<RGW>(part, lds[L.gam], lds, L, dec, lds + L.coef, nrec, P, yout, wave, lane);
     append_from_lds<KIND, N>(a, L, lds, b, hh, gq, nrec - 1, 0, (int)(nc % g.C), t);
   }
   if (t == 0) {
@@ -888,7 +911,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   }
 }
 
-template <int KIND, int N, int RBW>
+template <int KIND, int N, int RGW>
 __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -923,8 +946,8 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   sp.iq0 = sp.ik0;
   sp.iqs = sp.iks;
 
-  Frag<N, RBW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  Frag<N, RGW> F;
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
   __syncthreads();
 
   const float *xbase;
@@ -951,17 +974,17 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   }
 
   for (int tau = 0; tau < T; ++tau) {
-    float part[RBW];
+    float part[RGW];
     frag_dot(F, xbase + tau * N, lane, part);
     float *orow = a.out + (((int64_t)b * T + tau) * g.H + hh) * P;
-    write_rows<RBW>(part, lds[L.gam + tau], lds, L, dec ? dec + tau * cap : nullptr, lds + L.coef + tau * cap,
+    write_rows<RGW>(part, lds[L.gam + tau], lds, L, dec ? dec + tau * cap : nullptr, lds + L.coef + tau * cap,
                     hb + tau + 1, P, orow, wave, lane);
   }
   for (int tau = 0; tau < T; ++tau)
     append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, (int)((nc + tau) % g.C), t);
 }
 
-template <int KIND, int N, int RBW>
+template <int KIND, int N, int RGW>
 __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -983,8 +1006,8 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   float *tileS = a.s + (int64_t)tile * P * N;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, nrec, 0, 0);
-  Frag<N, RBW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  Frag<N, RGW> F;
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
   if (KIND == RSSM_KIND_MAMBA2) {
     if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
@@ -999,7 +1022,7 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   if (t == 0) a.n_ckpt[tile] = nc;
 }
 
-template <int KIND, int N, int RBW>
+template <int KIND, int N, int RGW>
 __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -1015,41 +1038,41 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   sp.iv0 = ((int64_t)b * g.H + hh) * P;
   sp.ik0 = ((int64_t)b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
-  Frag<N, RBW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load(F, tileS, P, wave, lane); });
+  Frag<N, RGW> F;
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
-  const int c = (lane >> 4) * 4;
+  const int c = frag_col(lane);
   const float al = lds[L.alpha];
   const float *kr = lds + L.K + c;
-  float u[RBW];
+  float u[RGW];
   if (KIND == RSSM_KIND_MAMBA2) {
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < RGW; ++i) {
       const int row = frag_row(wave, lane, i);
       u[i] = (row < P) ? lds[L.V + row] : 0.f;
     }
   } else {
-    float w[RBW];
+    float w[RGW];
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) w[i] = 0.f;
+    for (int i = 0; i < RGW; ++i) w[i] = 0.f;
 #pragma unroll
-    for (int f = 0; f < N / 16; ++f) {
-      const float4 kf = *(const float4 *)(kr + 16 * f);
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
-      for (int i = 0; i < RBW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
+      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
     }
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < RGW; ++i) {
       const int row = frag_row(wave, lane, i);
       const float vr = (row < P) ? lds[L.V + row] : 0.f;
-      u[i] = lds[L.beta] * (vr - al * quad_sum(w[i]));
+      u[i] = lds[L.beta] * (vr - al * oct_sum(w[i]));
     }
   }
 #pragma unroll
-  for (int f = 0; f < N / 16; ++f) {
-    const float4 kf = *(const float4 *)(kr + 16 * f);
+  for (int f = 0; f < N / 32; ++f) {
+    const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
-    for (int i = 0; i < RBW; ++i) {
+    for (int i = 0; i < RGW; ++i) {
       F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
       F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
       F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
@@ -1057,26 +1080,20 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
     }
   }
   frag_store(F, tileS, P, wave, lane);
-  float part[RBW];
+  float part[RGW];
   frag_dot(F, lds + L.q, lane, part);
-  float *yout = a.out + ((int64_t)b * g.H + hh) * P;
-#pragma unroll
-  for (int i = 0; i < RBW; ++i) {
-    const int row = frag_row(wave, lane, i);
-    const float y = quad_sum(part[i]);
-    if ((lane >> 4) == 0 && row < P) yout[row] = y;
-  }
+  write_row_sums<RGW>(part, P, a.out + ((int64_t)b * g.H + hh) * P, wave, lane);
 }
 
-template <int N, int RBW>
+template <int N, int RGW>
 __global__ __launch_bounds__(kThreads) void k_init(Args a) {
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int P = g.P;
-  Frag<N, RBW> F;
+  Frag<N, RGW> F;
   if (a.s0)
-    frag_load(F, a.s0 + (int64_t)tile * P * N, P, wave, lane);
+    frag_load<N, RGW, false>(F, a.s0 + (int64_t)tile * P * N, P, wave, lane);
   else
     frag_zero(F);
   frag_store(F, a.s + (int64_t)tile * P * N, P, wave, lane);
@@ -1089,35 +1106,43 @@ __global__ __launch_bounds__(kThreads) void k_init(Args a) {
   }
 }
 
-// Dispatch over the supported (N, RBW) instances; CALL(n, r) must return.
-#define RSSM_DISPATCH(N_, RBW_, CALL)                 \
+// Dispatch over the supported (N, RGW) instances (RGW * N <= 512, so a lane holds at most
+// 64 floats of the tile); CALL(n, r) must return.
+#define RSSM_DISPATCH(N_, RGW_, CALL)                 \
   switch (N_) {                                       \
     case 32:                                          \
-      switch (RBW_) {                                 \
+      switch (RGW_) {                                 \
         case 1: CALL(32, 1);                          \
         case 2: CALL(32, 2);                          \
         case 4: CALL(32, 4);                          \
         case 8: CALL(32, 8);                          \
+        case 16: CALL(32, 16);                        \
         default: break;                               \
       }                                               \
       break;                                          \
     case 64:                                          \
-      switch (RBW_) {                                 \
+      switch (RGW_) {                                 \
         case 1: CALL(64, 1);                          \
         case 2: CALL(64, 2);                          \
         case 4: CALL(64, 4);                          \
+        case 8: CALL(64, 8);                          \
         default: break;                               \
       }                                               \
       break;                                          \
     case 128:                                         \
-      switch (RBW_) {                                 \
+      switch (RGW_) {                                 \
         case 1: CALL(128, 1);                         \
         case 2: CALL(128, 2);                         \
+        case 4: CALL(128, 4);                         \
         default: break;                               \
       }                                               \
       break;                                          \
     case 256:                                         \
-      if (RBW_ == 1) CALL(256, 1);                    \
+      switch (RGW_) {                                 \
+        case 1: CALL(256, 1);                         \
+        case 2: CALL(256, 2);                         \
+        default: break;                               \
+      }                                               \
       break;                                          \
     default: break;                                   \
   }                                                   \

@@ -74,10 +74,11 @@ inline size_t lds_bytes(int kind, int cap, int T, int P, int N) {
   return (size_t)lds_layout(kind, cap, T, P, N).total * sizeof(float);
 }
 
-// Rows of a tile handled per wave: row blocks of 16, distributed over 4 waves.
-inline int rbw_for(int P) {
-  int rb = (P + 15) / 16;
-  int per = (rb + kWaves - 1) / kWaves;
+// Row groups of 8 handled per wave (the tile's P rows form ceil(P/8) groups over 4 waves),
+// rounded up to a power of two.
+inline int rgw_for(int P) {
+  int rg = (P + 7) / 8;
+  int per = (rg + kWaves - 1) / kWaves;
   int r = 1;
   while (r < per) r <<= 1;
   return r;
