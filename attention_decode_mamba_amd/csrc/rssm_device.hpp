@@ -853,16 +853,14 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
 
   Frag<N, RGW> F;
   RCopy<N, RGW> RCR;
-  // the tile is streamed with nontemporal loads when it is only read (non-fold steps); a
-  // fold step writes it back, and keeps ordinary loads
-  if (from_copy)
-    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+  // the tile is streamed with nontemporal loads (read once per step; on a fold step it is
+  // written back from registers)
+  stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+    if (from_copy)
       readcopy_load(RCR, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
-    });
-  else if (flush)
-    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
-  else
-    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+    else
+      frag_load<N, RGW, true>(F, tileS, P, wave, lane);
+  });
   __syncthreads();
 
   float *yout = a.out + ((int64_t)b * g.H + hh) * P;

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 
-#include "../../include/rssm.h"
+#include "rssm.h"
 
 namespace rssm {
 
