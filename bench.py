@@ -1,14 +1,20 @@
 """Benchmark of the ReplaySSM decode hot path on one MI355X.
 
-A step is one replay decode step (append + output-only replay, with the fold
-fused into the step that fills the 16-record window) for every sequence of one
-Mamba-2 layer at serving shape: batch 256, 128 heads, 64 x 128 fp32 state tiles
-(4 MiB per sequence), bf16 inputs.  Inputs for every timed step are generated
-up front and resident in HBM before the timed region.  The conventional
-read-modify-write kernel is timed on the same inputs as the comparison point,
-and the fp64 CPU oracle is timed on a bounded sample as a reported baseline.
+Default (the headline line): a step is one replay decode step (append +
+output-only replay, with the fold fused into the step that fills the 16-record
+window) for every sequence of one Mamba-2 layer at serving shape: batch 256,
+128 heads, 64 x 128 fp32 state tiles (4 MiB per sequence), bf16 inputs.  Inputs
+for every timed step are generated up front and resident in HBM before the
+timed region.  The conventional read-modify-write kernel is timed on the same
+inputs as the comparison point, and the fp64 CPU oracle is timed on a bounded
+sample as a reported baseline.  Prints one JSON line.
 
-Prints one JSON line (see the keys at the end of main()).
+Other measurements of the path (--workload):
+  gdn_b256          Gated DeltaNet replay decode, B=256, 32/16 heads, 128 x 128
+  m2_readcopy_b256  Mamba-2 replay decode with an fp8 or MXFP4 read copy (--read-copy)
+  m2_verify_b512    speculative verify(T=4) -> commit -> flush(16), B=512 (Mamba-2)
+  gdn_verify_b256   the same loop for Gated DeltaNet, B=256
+  --drift           read-copy output drift against the fp32 path over 4096 decode steps
 """
 from __future__ import annotations
 
@@ -41,40 +47,83 @@ def kernel_source_hash() -> str:
 
 
 # ----------------------------------------------------------------------------- byte model
+def _es(wl) -> int:
+    return 2 if wl.in_dtype == "bf16" else 4
+
+
+def _rec_bytes(wl):
+    """(bytes of one record per value head: alpha (+beta) + v, per key head: k)."""
+    s = _es(wl)
+    return s * (1 + wl.dv + (1 if wl.kind == "gdn" else 0)), s * wl.dk
+
+
+def _tile_read_bytes(wl, fold: bool) -> int:
+    PN = wl.dv * wl.dk
+    if fold or wl.read_copy == "none":
+        return 4 * PN
+    return PN + PN // 8 if wl.read_copy == "fp8" else PN // 2 + PN // 32
+
+
+def _copy_write_bytes(wl) -> int:
+    PN = wl.dv * wl.dk
+    return {"none": 0, "fp8": PN + PN // 8, "mxfp4": PN // 2 + PN // 32}[wl.read_copy]
+
+
 def step_bytes(wl, h: int) -> dict:
     """Algorithmic HBM bytes of one replay decode step over the whole batch, with h records
     in the window after the append (h == L: the fold step).  Per (sequence, head) tile:
-    checkpoint read 4PN (+ write 4PN on the fold step), the h-1 older ring records
-    (alpha, v per head; k per key head), the step inputs, the ring append (non-fold steps)
-    and the fp32 output row."""
-    s = 2 if wl.in_dtype == "bf16" else 4
+    checkpoint (or read-copy) read, on the fold step the checkpoint write (and the read-copy
+    write), the h-1 older ring records (alpha, beta, v per value head; k per key head), the
+    step inputs, the ring append (non-fold steps) and the fp32 output row."""
+    s = _es(wl)
     B, H, G, P, N = wl.batch, wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
-    gdn = wl.kind == "gdn"
-    flush = h >= wl.L
-    head_rec = s * (1 + P + (1 if gdn else 0))          # alpha (+beta) + v per value head
-    key_rec = s * N                                      # k per key head (ring reads need no q)
-    state_read = B * H * 4 * P * N
-    state_write = B * H * 4 * P * N if flush else 0
+    fold = h >= wl.L
+    head_rec, key_rec = _rec_bytes(wl)
+    state = B * H * _tile_read_bytes(wl, fold)
+    if fold:
+        state += B * H * (4 * P * N + _copy_write_bytes(wl))
     ring_read = (h - 1) * (B * H * head_rec + B * G * key_rec)
     inputs = B * H * head_rec + B * G * 2 * s * N
-    append = 0 if flush else inputs
+    append = 0 if fold else inputs
     out = B * H * 4 * P
-    total = state_read + state_write + ring_read + inputs + append + out
-    return dict(state=state_read + state_write, total=total)
+    return dict(state=state, total=state + ring_read + inputs + append + out)
 
 
 def conventional_bytes(wl) -> dict:
-    s = 2 if wl.in_dtype == "bf16" else 4
+    s = _es(wl)
     B, H, G, P, N = wl.batch, wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
+    head_rec, _ = _rec_bytes(wl)
     state = 2 * B * H * 4 * P * N
-    inputs = B * H * s * (1 + P) + B * G * 2 * s * N
+    inputs = B * H * head_rec + B * G * 2 * s * N
     return dict(state=state, total=state + inputs + B * H * 4 * P)
+
+
+def verify_bytes(wl, hs, T: int) -> dict:
+    """One verify launch: per tile the checkpoint read, the h committed ring records, T drafts
+    read and appended, T output rows.  hs: records in each sequence's window."""
+    s = _es(wl)
+    H, G, P, N = wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
+    head_rec, key_rec = _rec_bytes(wl)
+    nb = len(hs)
+    state = nb * H * 4 * P * N
+    ring = int(sum(hs)) * (H * head_rec + G * key_rec)
+    drafts = nb * T * (H * head_rec + G * 2 * s * N)
+    return dict(state=state, total=state + ring + 2 * drafts + nb * T * H * 4 * P)
+
+
+def flush_bytes(wl, hs_folded) -> dict:
+    """One flush launch: each folding sequence reads its h ring records and reads + writes
+    its checkpoint tiles."""
+    H, G, P, N = wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
+    head_rec, key_rec = _rec_bytes(wl)
+    state = len(hs_folded) * H * (8 * P * N + _copy_write_bytes(wl))
+    ring = int(sum(hs_folded)) * (H * head_rec + G * key_rec)
+    return dict(state=state, total=state + ring)
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 def _oracle_worker(args):
     wl, b, steps, barrier_at = args
-    import numpy as np  # noqa: F401
     from oracle import ReplayOracle
     from synth import decode_inputs, initial_state
     inps = [decode_inputs(wl, t, [b]) for t in range(steps)]
@@ -87,7 +136,7 @@ def _oracle_worker(args):
     return t0, time.time()
 
 
-def cpu_baseline(wl, n_seqs: int = 16, steps: int = 64) -> dict:
+def cpu_baseline(wl, n_seqs: int = 16, steps: int = 320) -> dict:
     """The fp64 oracle on a bounded sample: n_seqs sequences x steps decode steps, one
     sequence per worker process, all starting together; tokens/s = n_seqs*steps / wall."""
     from concurrent.futures import ProcessPoolExecutor
@@ -103,22 +152,31 @@ def cpu_baseline(wl, n_seqs: int = 16, steps: int = 64) -> dict:
     cpu = sum(e - s for s, e in spans)
     return {"value": n_seqs * steps / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"{n_seqs} sequences x {steps} decode steps of the same workload "
-                      f"(fp64 stepwise recurrence, all 128 heads), {cpu:.1f} s CPU over {workers} processes",
+                      f"(fp64 stepwise recurrence, all {wl.n_heads} heads), {cpu:.1f} s CPU over {workers} processes",
             "wall_s": round(wall, 3)}
 
 
-# ----------------------------------------------------------------------------- GPU run
-def _gen_inputs(wl, steps, torch):
-    """Per-step device inputs, generated in parallel over sequences and copied to HBM."""
+# ----------------------------------------------------------------------------- GPU helpers
+def _to_dev(arrs, torch):
     import numpy as np
+    out = {}
+    for k, v in arrs.items():
+        if v is None:
+            out[k] = None
+        else:
+            a = np.ascontiguousarray(v)
+            out[k] = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    return out
+
+
+def _gen_inputs(wl, steps, torch, drafts_T=0):
+    """Per-step device inputs (decode records, or T drafts per sequence), generated in
+    parallel over sequences and copied to HBM."""
     from synth.stream import StepSource
     out = []
     with StepSource(wl, range(wl.batch)) as src:
         for t in range(steps):
-            d = src.decode(t)
-            out.append({k: (torch.from_numpy(np.ascontiguousarray(v).view(np.int16) if v.dtype == np.uint16
-                                              else np.ascontiguousarray(v)).cuda()
-                            if v is not None else None) for k, v in d.items()})
+            out.append(_to_dev(src.drafts(t, drafts_T) if drafts_T else src.decode(t), torch))
     return out
 
 
@@ -127,30 +185,75 @@ def _s0_device(wl, torch):
     from concurrent.futures import ProcessPoolExecutor
     from synth import initial_state
     from synth.gen import default_workers
-    chunks = np.array_split(np.arange(wl.batch), default_workers())
+    chunks = [c for c in np.array_split(np.arange(wl.batch), default_workers()) if len(c)]
     s0 = torch.empty(wl.batch, wl.n_heads, wl.dv, wl.dk, dtype=torch.float32, device="cuda")
     with ProcessPoolExecutor(max_workers=len(chunks)) as ex:
         for idx, arr in zip(chunks, ex.map(initial_state, [wl] * len(chunks), [list(c) for c in chunks])):
-            if len(idx):
-                s0[int(idx[0]): int(idx[-1]) + 1] = torch.from_numpy(arr).cuda()
+            s0[int(idx[0]): int(idx[-1]) + 1] = torch.from_numpy(arr).cuda()
     return s0
 
 
-def run(args) -> dict:
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+class _Timer:
+    """Elapsed time of a launch sequence on one stream (start/end events only), or an event
+    pair around every launch."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def total_ms(self, fn, n):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        a.record(self.stream)
+        for i in range(n):
+            fn(i)
+        b.record(self.stream)
+        t.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def per_launch_ms(self, fns, n):
+        """fns: list of callables(i); returns per-callable lists of durations."""
+        t = self.torch
+        ev = [[(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in fns] for _ in range(n)]
+        t.cuda.synchronize()
+        for i in range(n):
+            for j, fn in enumerate(fns):
+                ev[i][j][0].record(self.stream)
+                fn(i)
+                ev[i][j][1].record(self.stream)
+        t.cuda.synchronize()
+        return [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n)] for j in range(len(fns))]
+
+
+def _stream_copy_gbps(R, torch, stream, sh):
+    nbytes = COPY_BYTES
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    R.rssm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        R.rssm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 5 * 2 * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+# ----------------------------------------------------------------------------- decode
+def run_decode(args, wl, with_conventional=True) -> dict:
     import torch
     from attention_decode_mamba_amd import rssm as R
     from attention_decode_mamba_amd.state import DeviceState, config_of
-    from synth import get_workload
 
-    wl = get_workload(WORKLOAD)
-    if args.batch:
-        wl = wl.replace(batch=args.batch)
     K, W = args.steps, args.warmup
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-
-    print(f"[bench] generating inputs for {W + K} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: generating inputs for {W + K} steps", file=sys.stderr, flush=True)
     t0 = time.time()
     s0 = _s0_device(wl, torch)
     inputs = _gen_inputs(wl, W + K, torch)
@@ -159,52 +262,23 @@ def run(args) -> dict:
     cfg = config_of(wl)
     ds = DeviceState(cfg)
     ds.init(s0, sh)
-    conv = s0.clone()
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
 
     def replay(t):
         d = inputs[t]
-        R.rssm_decode_step(cfg, ds.st, d["alpha"].data_ptr(), None, d["v"].data_ptr(), d["k"].data_ptr(),
-                           d["q"].data_ptr(), y.data_ptr(), sh)
+        R.rssm_decode_step(cfg, ds.st, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                           y.data_ptr(), sh)
 
-    def conventional(t):
-        d = inputs[t]
-        R.rssm_decode_step_conventional(cfg, conv.data_ptr(), d["alpha"].data_ptr(), None, d["v"].data_ptr(),
-                                        d["k"].data_ptr(), d["q"].data_ptr(), y.data_ptr(), sh)
-
-    def timed(fn, first, per_launch):
-        """Elapsed ms of K launches (start/end events only), or per-launch durations."""
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if not per_launch:
-            torch.cuda.synchronize()
-            start.record(stream)
-            for i in range(K):
-                fn(first + i)
-            end.record(stream)
-            torch.cuda.synchronize()
-            return start.elapsed_time(end), None
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        torch.cuda.synchronize()
-        for i in range(K):
-            ev[i][0].record(stream)
-            fn(first + i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return None, [a.elapsed_time(b) for a, b in ev]
-
-    # timed region: K steps bracketed by synchronisation, no events in between
+    tm = _Timer(torch, stream)
     for t in range(W):
         replay(t)
-    total_ms, _ = timed(replay, W, False)
-    # the same K launches again (same window phases) with an event pair around each launch
-    _, per = timed(lambda t: replay(W + (t - W) % K), W + K, True)
+    # timed region: K steps bracketed by synchronisation, no events in between
+    total_ms = tm.total_ms(lambda i: replay(W + i), K)
+    # the same K launches again (same inputs; window phases continue from W + K), with an
+    # event pair around each launch: the per-launch durations of the roofline
+    (per,) = tm.per_launch_ms([lambda i: replay(W + i)], K)
     assert ds.error() == 0
-    for t in range(W):
-        conventional(t)
-    conv_ms, _ = timed(conventional, W, False)
 
-    # exact algorithmic bytes: launch i of the timed region sits at window phase
-    # h = ((W + i) % L) + 1 records after the append; the per-launch pass continues at W + K
     hs1 = [((W + i) % wl.L) + 1 for i in range(K)]
     alg_total = sum(step_bytes(wl, h)["total"] for h in hs1)
     alg_state = sum(step_bytes(wl, h)["state"] for h in hs1)
@@ -213,50 +287,15 @@ def run(args) -> dict:
     kern_ms = sum(per)
     fold = [p for p, h in zip(per, hs) if h == wl.L]
     nonfold = [p for p, h in zip(per, hs) if h != wl.L]
-    cb = conventional_bytes(wl)
-
-    # achievable bandwidth of a plain streaming copy (context for the roofline fraction)
-    nbytes = COPY_BYTES
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    R.rssm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
-    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cs.record(stream)
-    for _ in range(5):
-        R.rssm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
-    ce.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * nbytes / (cs.elapsed_time(ce) * 1e-3) / 1e9
-    del src, dst
-
+    nf_bytes = [step_bytes(wl, h)["total"] for h in hs if h != wl.L]
+    achieved = alg_launch / (kern_ms / K * 1e-3) / 1e9
     B = wl.batch
-    avg_launch_s = kern_ms / K * 1e-3
-    achieved = alg_launch / avg_launch_s / 1e9
-    traffic = None
-    if os.path.exists(PROFILE_SUMMARY):
-        with open(PROFILE_SUMMARY) as f:
-            prof = json.load(f)
-        if prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("batch") == B:
-            traffic = prof.get("traffic_bytes_per_launch")
     res = {
-        "metric": METRIC,
         "value": B * K / (total_ms * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
         "ms_per_step": total_ms / K,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"mamba2_replay_decode_b{B}_h128_p64_n128_bf16in_fp32state_L16",
-                   "batch": B, "heads": wl.n_heads, "dv": wl.dv, "dk": wl.dk, "window": wl.L,
-                   "in_dtype": wl.in_dtype, "state_dtype": "fp32", "parallelism": "single_gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "k_decode<mamba2, N=128, RGW=2>",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
                      "algorithmic_bytes_per_launch": alg_launch},
         "state_GBps": alg_state / (total_ms * 1e-3) / 1e9,
         "total_GBps": alg_total / (total_ms * 1e-3) / 1e9,
@@ -264,15 +303,196 @@ def run(args) -> dict:
         "kernel_ms_per_launch": kern_ms / K,
         "fold_step_ms": sum(fold) / max(len(fold), 1),
         "nonfold_step_ms": sum(nonfold) / max(len(nonfold), 1),
-        "conventional": {"tokens_per_s": B * K / (conv_ms * 1e-3), "ms_per_step": conv_ms / K,
-                         "state_GBps": cb["state"] / (conv_ms / K * 1e-3) / 1e9,
-                         "total_GBps": cb["total"] / (conv_ms / K * 1e-3) / 1e9},
-        "speedup_vs_conventional": conv_ms / total_ms,
-        "stream_copy_GBps": copy_gbps,
+        "nonfold_GBps": (sum(nf_bytes) / len(nf_bytes)) / (sum(nonfold) / len(nonfold) * 1e-3) / 1e9
+        if nonfold else None,
     }
+    if with_conventional:
+        conv = s0.clone()
+
+        def conventional(t):
+            d = inputs[t]
+            R.rssm_decode_step_conventional(cfg, conv.data_ptr(), _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
+                                            _p(d["k"]), _p(d["q"]), y.data_ptr(), sh)
+
+        for t in range(W):
+            conventional(t)
+        conv_ms = tm.total_ms(lambda i: conventional(W + i), K)
+        cb = conventional_bytes(wl)
+        res["conventional"] = {"tokens_per_s": B * K / (conv_ms * 1e-3), "ms_per_step": conv_ms / K,
+                               "state_GBps": cb["state"] / (conv_ms / K * 1e-3) / 1e9,
+                               "total_GBps": cb["total"] / (conv_ms / K * 1e-3) / 1e9}
+        res["speedup_vs_conventional"] = conv_ms / total_ms
+    res["stream_copy_GBps"] = _stream_copy_gbps(R, torch, stream, sh)
     return res
 
 
+def headline(args) -> dict:
+    from synth import get_workload
+    wl = get_workload(WORKLOAD)
+    if args.batch:
+        wl = wl.replace(batch=args.batch)
+    r = run_decode(args, wl)
+    traffic = None
+    if os.path.exists(PROFILE_SUMMARY):
+        with open(PROFILE_SUMMARY) as f:
+            prof = json.load(f)
+        if prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("batch") == wl.batch:
+            traffic = prof.get("traffic_bytes_per_launch")
+    r["roofline"]["traffic"] = traffic
+    r["roofline"]["kernel"] = "k_decode<mamba2, N=128, RGW=2>"
+    out = {"metric": METRIC, "value": r.pop("value"), "unit": r.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": r.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": f"mamba2_replay_decode_b{wl.batch}_h128_p64_n128_bf16in_fp32state_L16",
+                      "batch": wl.batch, "heads": wl.n_heads, "dv": wl.dv, "dk": wl.dk, "window": wl.L,
+                      "in_dtype": wl.in_dtype, "state_dtype": "fp32", "parallelism": "single_gpu"}}
+    out.update(r)
+    return out
+
+
+# ----------------------------------------------------------------------------- verify loop
+def run_verify(args, wl) -> dict:
+    """verify(T) -> commit(a) -> flush(L) per step; a ~ U{0..T} per sequence and step."""
+    import numpy as np
+    import torch
+    from attention_decode_mamba_amd import rssm as R
+    from attention_decode_mamba_amd.state import DeviceState, config_of
+    from synth import accept_counts
+
+    T = wl.t_max
+    K, W = args.steps, args.warmup
+    distinct = min(args.distinct, W + K)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    print(f"[bench] {wl.name}: generating {distinct} distinct draft steps (cycled)", file=sys.stderr, flush=True)
+    s0 = _s0_device(wl, torch)
+    drafts = _gen_inputs(wl, distinct, torch, drafts_T=T)
+    accept = [accept_counts(wl, s, T) for s in range(W + K)]
+    accept_dev = [torch.from_numpy(a).cuda() for a in accept]
+    cfg = config_of(wl)
+    ds = DeviceState(cfg)
+    ds.init(s0, sh)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+
+    def verify(s):
+        d = drafts[s % distinct]
+        R.rssm_verify(cfg, ds.st, T, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                      o.data_ptr(), sh)
+
+    def commit(s):
+        R.rssm_commit(cfg, ds.st, accept_dev[s].data_ptr(), T, sh)
+
+    def flush(s):
+        R.rssm_flush(cfg, ds.st, wl.L, sh)
+
+    def step(s):
+        verify(s)
+        commit(s)
+        flush(s)
+
+    # host-side cursor bookkeeping for the byte counts (the same integer policy as the kernels)
+    h = np.zeros(wl.batch, np.int64)
+    hist = []
+    for s in range(W + K):
+        h_before = h.copy()
+        h = h + accept[s]
+        folded = h >= wl.L
+        hist.append((h_before, h[folded].copy()))
+        h[folded] = 0
+
+    tm = _Timer(torch, stream)
+    for s in range(W):
+        step(s)
+    total_ms = tm.total_ms(lambda i: step(W + i), K)
+    assert ds.error() == 0
+    committed = int(sum(int(accept[W + i].sum()) for i in range(K)))
+    # per-kernel durations on a second pass over the same steps (cursor restarted)
+    ds.init(s0, sh)
+    for s in range(W):
+        step(s)
+    pv, pc, pf = tm.per_launch_ms([lambda i: verify(W + i), lambda i: commit(W + i), lambda i: flush(W + i)], K)
+    assert ds.error() == 0
+    vb = [verify_bytes(wl, hist[W + i][0], T) for i in range(K)]
+    fb = [flush_bytes(wl, hist[W + i][1]) for i in range(K)]
+    v_ach = sum(b["total"] for b in vb) / (sum(pv) * 1e-3) / 1e9
+    f_ach = sum(b["total"] for b in fb) / (sum(pf) * 1e-3) / 1e9
+    return {
+        "metric": f"speculative verify->commit->flush, committed tokens/s ({wl.name}, T={T})",
+        "value": committed / (total_ms * 1e-3), "unit": "committed tokens/s",
+        "ms_per_step": total_ms / K, "steps": K, "warmup": W, "data": "synthetic",
+        "draft_inputs": f"{distinct} distinct draft batches cycled; accepted prefix ~ U{{0..{T}}} per step",
+        "mean_accept": committed / (K * wl.batch),
+        "verify": {"ms": sum(pv) / K, "GBps": v_ach, "frac": v_ach / PEAK_HBM_GBPS,
+                   "bytes_per_launch": sum(b["total"] for b in vb) / K},
+        "commit": {"ms": sum(pc) / K},
+        "flush": {"ms": sum(pf) / K, "GBps": f_ach, "frac": f_ach / PEAK_HBM_GBPS,
+                  "bytes_per_launch": sum(b["total"] for b in fb) / K,
+                  "sequences_folded_per_step": sum(len(hist[W + i][1]) for i in range(K)) / K},
+        "roofline": {"bound": "hbm", "kernel": "k_verify", "achieved": v_ach, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": v_ach / PEAK_HBM_GBPS},
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.n_heads, "qk_heads": wl.n_qk_heads,
+                   "dv": wl.dv, "dk": wl.dk, "T": T, "window": wl.L, "capacity": wl.capacity},
+    }
+
+
+# ----------------------------------------------------------------------------- read-copy drift
+def run_drift(args) -> dict:
+    """Output drift of the fp8 / MXFP4 read copy against the fp32 path on the same inputs:
+    normwise relative error per output vector, per 256-step bin, over the decode steps."""
+    import numpy as np
+    import torch
+    from attention_decode_mamba_amd import rssm as R
+    from attention_decode_mamba_amd.state import DeviceState, config_of
+    from synth import get_workload
+    from synth.stream import StepSource
+
+    steps = args.drift_steps
+    wl = get_workload("m2_readcopy_b256").replace(batch=args.drift_batch)
+    torch.cuda.set_device(0)
+    sh = torch.cuda.current_stream().cuda_stream
+    s0 = _s0_device(wl, torch)
+    states = {}
+    for fmt in ("none", "fp8", "mxfp4"):
+        ds = DeviceState(config_of(wl.replace(read_copy=fmt)))
+        ds.init(s0, sh)
+        states[fmt] = ds
+    ys = {f: torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda") for f in states}
+    bins = {f: [] for f in ("fp8", "mxfp4")}
+    cur = {f: [] for f in ("fp8", "mxfp4")}
+    with StepSource(wl, range(wl.batch)) as src:
+        for t in range(steps):
+            d = _to_dev(src.decode(t), torch)
+            for f, ds in states.items():
+                R.rssm_decode_step(ds.cfg, ds.st, _p(d["alpha"]), None, _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                                   ys[f].data_ptr(), sh)
+            ref = ys["none"].double()
+            den = ref.abs().amax(dim=-1).clamp_min(1e-30)
+            for f in ("fp8", "mxfp4"):
+                e = (ys[f].double() - ref).abs().amax(dim=-1) / den
+                cur[f].append((float(e.mean()), float(e.max())))
+            if (t + 1) % 256 == 0:
+                for f in ("fp8", "mxfp4"):
+                    arr = np.array(cur[f])
+                    bins[f].append({"steps": [t - 255, t], "mean": float(arr[:, 0].mean()),
+                                    "max": float(arr[:, 1].max())})
+                    cur[f] = []
+                print(f"[drift] step {t + 1}/{steps}", file=sys.stderr, flush=True)
+    for ds in states.values():
+        assert ds.error() == 0
+    out = {"metric": "read-copy output drift vs the fp32 path (normwise relative error per output vector)",
+           "config": {"workload": wl.name, "batch": wl.batch, "steps": steps, "window": wl.L}}
+    for f in ("fp8", "mxfp4"):
+        means = np.array([b["mean"] for b in bins[f]])
+        x = np.arange(len(means))
+        slope = float(np.polyfit(x, means, 1)[0]) if len(means) > 1 else 0.0
+        out[f] = {"bins": bins[f], "mean_of_means": float(means.mean()),
+                  "fitted_slope_per_bin": slope, "slope_over_mean": slope / float(means.mean())}
+    return out
+
+
+# ----------------------------------------------------------------------------- counters
 def _read_counter_csv(path):
     """rocprofv3 counter_collection CSV -> {dispatch_id: (kernel_name, {counter: value})}."""
     import csv
@@ -288,7 +508,7 @@ def _read_counter_csv(path):
     return out
 
 
-def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps):
+def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, warmup):
     """Per-launch HBM traffic of the decode and conventional kernels from two --pmc runs
     (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
     reads for the streaming copy of COPY_BYTES bytes."""
@@ -299,8 +519,7 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps):
     write = _read_counter_csv(write_csv)
 
     def per_kernel(table, counter, key):
-        vals = [c.get(counter, 0.0) for n, c in table.values() if key in n]
-        return vals
+        return [c.get(counter, 0.0) for n, c in table.values() if key in n]
 
     cf = per_kernel(fetch, "FETCH_SIZE", "k_stream_copy")
     cw = per_kernel(write, "WRITE_SIZE", "k_stream_copy")
@@ -320,9 +539,10 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps):
         res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
                       "write_mib_per_dispatch_min_max": [min(w) / 1024.0 * fw, max(w) / 1024.0 * fw]}
-    W = 16
-    hs = [((W + i) % wl.L) + 1 for i in range(steps)]
-    alg = sum(step_bytes(wl, h)["total"] for h in hs) / steps
+    # every decode dispatch of the run: warmup, timed pass and per-launch pass
+    n = warmup + 2 * steps
+    hs = [(i % wl.L) + 1 for i in range(n)]
+    alg = sum(step_bytes(wl, h)["total"] for h in hs) / n
     res["algorithmic_bytes_per_launch"] = alg
     if "replay_decode" in res:
         r = res["replay_decode"]
@@ -338,7 +558,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--batch", type=int, default=0, help="override the batch (default: 256)")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch of the headline workload")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=[WORKLOAD, "gdn_b256", "m2_readcopy_b256", "m2_verify_b512", "gdn_verify_b256"])
+    ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
+    ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
+    ap.add_argument("--drift", action="store_true", help="read-copy drift report and exit")
+    ap.add_argument("--drift-steps", type=int, default=4096)
+    ap.add_argument("--drift-batch", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -347,7 +574,7 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], PROFILE_SUMMARY,
-                               args.counter_command, args.batch or 256, args.steps)
+                               args.counter_command, args.batch or 256, args.steps, args.warmup)
         print(json.dumps(r, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -358,12 +585,29 @@ def main():
     if args.cpu_baseline_only:
         print(json.dumps(cpu_baseline(get_workload(WORKLOAD))))
         return
-    res = run(args)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(get_workload(WORKLOAD))
+    if args.drift:
+        print(json.dumps(run_drift(args)))
+        return
+    if args.workload == WORKLOAD:
+        res = headline(args)
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = cpu_baseline(get_workload(WORKLOAD))
+        else:
+            res["cpu_baseline"] = None
+        print(json.dumps(res))
+        return
+    if args.workload in ("m2_verify_b512", "gdn_verify_b256"):
+        wl = get_workload("m2_verify_b512" if args.workload == "m2_verify_b512" else "gdn_b256")
+        res = run_verify(args, wl)
     else:
-        res["cpu_baseline"] = None
+        wl = get_workload(args.workload)
+        if args.workload == "m2_readcopy_b256":
+            wl = wl.replace(read_copy=args.read_copy)
+        res = run_decode(args, wl)
+        res["metric"] = f"replay decode tokens/s ({wl.name}, read copy {wl.read_copy})"
+        res["config"] = {"workload": wl.name, "batch": wl.batch, "heads": wl.n_heads, "qk_heads": wl.n_qk_heads,
+                         "dv": wl.dv, "dk": wl.dk, "window": wl.L, "read_copy": wl.read_copy}
     print(json.dumps(res))
 
 
