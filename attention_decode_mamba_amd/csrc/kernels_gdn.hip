@@ -11,21 +11,27 @@ inline dim3 grid_of(const Args &a) { return dim3((unsigned)(a.g.B * a.g.H)); }
 
 hipError_t launch_decode_gdn(const Args &a, hipStream_t s) {
   const size_t lds = lds_bytes(kKind, a.g.C + 1, 1, a.g.P, a.g.N);
-  if (a.g.read_copy != RSSM_READ_NONE) {
 #define CALL(n, r)                                                                             \
   {                                                                                            \
-    hipLaunchKernelGGL((k_decode<kKind, n, r, true>), grid_of(a), dim3(kThreads), lds, s, a);  \
+    hipLaunchKernelGGL((k_decode<kKind, n, r, F>), grid_of(a), dim3(kThreads), lds, s, a);     \
     return hipGetLastError();                                                                  \
   }
-    RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
-#undef CALL
+  switch (a.g.read_copy) {
+    case RSSM_READ_NONE: {
+      constexpr int F = RSSM_READ_NONE;
+      RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
+    }
+    case RSSM_READ_FP8: {
+      constexpr int F = RSSM_READ_FP8;
+      RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
+    }
+    case RSSM_READ_MXFP4: {
+      constexpr int F = RSSM_READ_MXFP4;
+      RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
+    }
+    default:
+      return hipErrorInvalidValue;
   }
-#define CALL(n, r)                                                                             \
-  {                                                                                            \
-    hipLaunchKernelGGL((k_decode<kKind, n, r, false>), grid_of(a), dim3(kThreads), lds, s, a); \
-    return hipGetLastError();                                                                  \
-  }
-  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
 #undef CALL
 }
 

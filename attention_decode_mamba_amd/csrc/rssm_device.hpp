@@ -39,27 +39,44 @@ __device__ __forceinline__ int tile_of_block(int ntiles) {
   return bid;
 }
 
-// Sum / max over the 8 lanes that share a row (lanes differing in bits 0..2).
+// Cross-lane moves inside a DPP row of 16 lanes (no LDS round trip): quad permutation
+// [1,0,3,2] (lane ^ 1), quad permutation [2,3,0,1] (lane ^ 2), half-row mirror (lane i of
+// each 8 takes lane 7 - i) and row mirror (lane i of each 16 takes lane 15 - i).  Every
+// source lane lies in the same row, so all lanes of the row must be active.
+enum : int { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum / max over the 8 lanes that share a row (lanes l with equal l / 8).  After the two
+// quad steps every lane holds its quad's result; the half-row mirror pairs each lane with
+// a lane of the other quad.  Each step adds commuted pairs, so all 8 lanes end bitwise equal.
 __device__ __forceinline__ float oct_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowHalfMirror>(v);
   return v;
 }
 
 __device__ __forceinline__ float oct_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
   return v;
 }
 
+// Sum over the 16 lanes of a DPP row (lanes l with equal l / 16).
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 1);
+  v = oct_sum(v);
+  v += dpp_mov<kDppRowMirror>(v);
   return v;
+}
+
+// Value of x in lane m (m uniform across the wave).
+__device__ __forceinline__ float lane_value(float x, int m) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), m));
 }
 
 // x_l <- prod_{m >= l} x_m over the 64 lanes of the wave (all lanes must be active).
@@ -254,42 +271,47 @@ struct RCopy {
   static constexpr int NCH = N / 16;
   static constexpr int CI = (NCH + 7) / 8;
   uint4 raw[RGW][CI];
-  float sc[RGW][CI];
+  uint32_t scb[RGW][CI];     // block scale as stored: fp32 bits (fp8) or the E8M0 byte (MXFP4)
 };
 
+// All loads are issued back to back: the format branch is outside the loops and nothing
+// is decoded here, so no load waits for another (decoding happens in readcopy_dot).
 template <int N, int RGW>
 __device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const uint8_t *__restrict__ codes,
                                               const uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
                                               int lane) {
   constexpr int NCH = RCopy<N, RGW>::NCH;
   const int c8 = lane & 7;
-  const bool fp8 = fmt == RSSM_READ_FP8;
+  if (fmt == RSSM_READ_FP8) {
 #pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    int row = frag_row(wave, lane, i);
-    row = row < P ? row : P - 1;                 // ragged rows: a copy of row P - 1, never stored
-    const int64_t rowi = tile * P + row;
+    for (int i = 0; i < RGW; ++i) {
+      int row = frag_row(wave, lane, i);
+      row = row < P ? row : P - 1;               // ragged rows: a copy of row P - 1, never stored
+      const int64_t rowi = tile * P + row;
 #pragma unroll
-    for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
-      const int k = c8 + 8 * ci;
-      const int kc = k < NCH ? k : NCH - 1;
-      uint4 w;
-      float sc;
-      if (fp8) {
+      for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
+        const int k = c8 + 8 * ci;
+        const int kc = k < NCH ? k : NCH - 1;
         const f4v v = __builtin_nontemporal_load((const f4v *)(codes + rowi * N + 16 * kc));
-        w = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
-        sc = ((const float *)scales)[rowi * (N / 32) + kc / 2];
-      } else {
+        R.raw[i][ci] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                  __float_as_uint(v[3]));
+        R.scb[i][ci] = ((const uint32_t *)scales)[rowi * (N / 32) + kc / 2];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      int row = frag_row(wave, lane, i);
+      row = row < P ? row : P - 1;
+      const int64_t rowi = tile * P + row;
+#pragma unroll
+      for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
+        const int k = c8 + 8 * ci;
+        const int kc = k < NCH ? k : NCH - 1;
         const uint2 v = *(const uint2 *)(codes + rowi * (N / 2) + 8 * kc);
-        w = make_uint4(v.x, v.y, 0, 0);
-        sc = __uint_as_float((uint32_t)scales[rowi * (N / 32) + kc / 2] << 23);   // 2^(e8m0 - 127)
+        R.raw[i][ci] = make_uint4(v.x, v.y, 0, 0);
+        R.scb[i][ci] = scales[rowi * (N / 32) + kc / 2];
       }
-      if (k >= NCH) {                             // no such chunk in this row: contributes nothing
-        w = make_uint4(0, 0, 0, 0);
-        sc = 0.f;
-      }
-      R.raw[i][ci] = w;
-      R.sc[i][ci] = sc;
     }
   }
 }
@@ -305,9 +327,12 @@ __device__ __forceinline__ void readcopy_dot(const RCopy<N, RGW> &R, int fmt, co
 #pragma unroll
     for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
       const int k = c8 + 8 * ci;
-      const float *xp = x + 16 * (k < RCopy<N, RGW>::NCH ? k : 0);
-      const uint4 w = R.raw[i][ci];
-      const float sc = R.sc[i][ci];
+      const bool has = k < RCopy<N, RGW>::NCH;   // lanes past the row's chunks contribute nothing
+      const float *xp = x + 16 * (has ? k : 0);
+      const uint4 w = has ? R.raw[i][ci] : make_uint4(0, 0, 0, 0);
+      const uint32_t sb = R.scb[i][ci];
+      // fp8: the fp32 scale; MXFP4: 2^(e8m0 - 127) is the e8m0 byte in the fp32 exponent field
+      const float sc = has ? __uint_as_float(fmt == RSSM_READ_FP8 ? sb : sb << 23) : 0.f;
       if (fmt == RSSM_READ_FP8) {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         float d = 0.f;
@@ -693,7 +718,7 @@ __device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, i
   float *cc = lds + L.cc + tau * cap;
   float x = (lane < n) ? coef[lane] : 0.f;
   for (int m = n - 1; m >= 0; --m) {
-    const float cm = __shfl(x, m);
+    const float cm = lane_value(x, m);
     if (lane < m) x = fmaf(-beta[m] * cm, gram[lane * (cap + 1) + m], x);
   }
   float p = (lane < n) ? alpha[lane] : 1.f;
@@ -822,10 +847,12 @@ __device__ __forceinline__ void write_rows(const float (&part)[RGW], float G, co
 // ================================================================ kernels
 
 // U: staging chunks per thread per round (2 covers a 17-record Mamba-2 window at 64 x 128
-// in bf16 in one round).  RC: the kernel serves non-fold steps from the read copy.
-template <int KIND, int N, int RGW, bool RC>
+// in bf16 in one round).  RCF: the read-copy format (RSSM_READ_*); with a copy the kernel
+// serves non-fold steps from it.
+template <int KIND, int N, int RGW, int RCF>
 __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   constexpr int U = (KIND == RSSM_KIND_GDN || RGW > 2) ? 4 : 2;
+  constexpr bool RC = RCF != RSSM_READ_NONE;
   extern __shared__ float lds[];
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
@@ -857,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   // written back from registers)
   stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
     if (from_copy)
-      readcopy_load(RCR, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+      readcopy_load(RCR, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
     else
       frag_load<N, RGW, true>(F, tileS, P, wave, lane);
   });
@@ -873,7 +900,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       fold_gdn(F, lds, L, nrec, P, wave, lane);
     }
     frag_store(F, tileS, P, wave, lane);
-    if (RC) frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+    if (RC) frag_store_read_copy(F, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
     float part[RGW];
     frag_dot(F, lds + L.q, lane, part);
     write_row_sums<RGW>(part, P, yout, wave, lane);
@@ -897,7 +924,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     }
     float part[RGW];
     if (from_copy)
-      readcopy_dot(RCR, g.read_copy, x, lane, part);
+      readcopy_dot(RCR, RCF, x, lane, part);
     else
       frag_dot(F, x, lane, part);
     write_rows<RGW>(part, lds[L.gam], lds, L, dec, lds + L.coef, nrec, P, yout, wave, lane);
