@@ -1,5 +1,6 @@
 // Host layer of the C ABI (include/rssm.h): argument validation, buffer sizing,
 // geometry setup and kernel launch.  Nothing is enqueued when validation fails.
+#include <algorithm>
 #include <string.h>
 
 #include "rssm_internal.hpp"
@@ -24,6 +25,11 @@ int check_cfg(const rssm_config *c) {
   if (c->L < 1 || c->t_max < 1 || c->t_max > kMaxDrafts) return RSSM_E_RANGE;
   if (c->capacity < c->L + c->t_max - 1 || c->capacity > kMaxCapacity) return RSSM_E_SHAPE;
   if ((int64_t)c->batch * c->n_heads > (int64_t)(1 << 30)) return RSSM_E_SHAPE;
+  // ring and input element indices are computed in 32 bits on the device
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t rows_v = (int64_t)c->batch * c->n_heads, rows_k = (int64_t)c->batch * c->n_qk_heads;
+  const int64_t slots = std::max<int64_t>(c->capacity, c->t_max);
+  if (rows_v * slots * c->dv >= lim || rows_k * slots * c->dk >= lim) return RSSM_E_SHAPE;
   if (lds_bytes(c->kind, c->capacity + 1, 1, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
   if (lds_bytes(c->kind, c->capacity, c->t_max, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
   return RSSM_OK;
@@ -59,6 +65,13 @@ Geom make_geom(const rssm_config *c) {
   g.L = c->L;
   g.C = c->capacity;
   g.bf16 = c->in_dtype == RSSM_DTYPE_BF16;
+  {
+    // log2 of the 16-byte chunks per value row (P * element size / 16), or -1 when that is
+    // not a power of two (or not whole)
+    const int bytes = c->dv * (g.bf16 ? 2 : 4);
+    const int cpv = bytes / 16;
+    g.cpv_lg = (bytes % 16 == 0 && cpv > 0 && (cpv & (cpv - 1)) == 0) ? __builtin_ctz(cpv) : -1;
+  }
   g.read_copy = c->read_copy;
   int64_t off[5], total;
   ring_layout(c, off, &total);

@@ -377,14 +377,29 @@ __device__ __forceinline__ void readcopy_dot(const RCopy<N, RGW> &R, int fmt, co
 // are input records j - n_ring (element offsets iv0/ik0 + (j - n_ring) * stride).
 // Queries are nq input rows (iq0 + r * iqs).  Everything lands in LDS as fp32:
 // alpha[j], beta[j], V[j][P], K[j][N+4], Q[r][N].
+// Element indices are 32-bit: the host bounds every ring region and input below 2^31
+// elements.
 struct StageSpec {
   int nrec, n_ring, slot0, C, P, N, nq, bf16;
+  int cpv_lg;                            // log2 of 16-byte chunks per value row, or -1
   const uint8_t *rA, *rB, *rV, *rK;      // ring regions
-  int64_t hrow, krow;                    // ring row (slot 0) of this value head / key head
+  int hrow, krow;                        // ring row (slot 0) of this value head / key head
   const void *iA, *iB, *iV, *iK, *iQ;    // inputs
-  int64_t ia0, ias, iv0, ivs, ik0, iks, iq0, iqs;
+  int ia0, ias, iv0, ivs, ik0, iks, iq0, iqs;
   float *A, *Bt, *V, *K, *Q;             // LDS
 };
+
+// x mod C for a cursor position x >= 0 (a 32-bit remainder while x fits in 32 bits).
+__device__ __forceinline__ int ring_mod(int64_t x, int C) {
+  if ((uint64_t)x < ((uint64_t)1 << 32)) return (int)((uint32_t)x % (uint32_t)C);
+  return (int)(x % C);
+}
+
+// (s0 + d) mod C for 0 <= s0 < C and 0 <= d <= C.
+__device__ __forceinline__ int ring_add(int s0, int d, int C) {
+  const int s = s0 + d;
+  return s >= C ? s - C : s;
+}
 
 __device__ __forceinline__ int ring_slot(const StageSpec &sp, int j) {
   int s = sp.slot0 + j;
@@ -416,12 +431,12 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
   if (with_scalars) {
     const int j = t < sp.nrec ? t : sp.nrec - 1;
     const bool ring = j < sp.n_ring;
-    const int64_t ri = sp.hrow + ring_slot(sp, j);
-    const int64_t ii = sp.ia0 + (int64_t)(j - sp.n_ring) * sp.ias;
-    const uint8_t *pa = ring ? sp.rA + ri * es : (const uint8_t *)sp.iA + ii * es;
+    const int ri = sp.hrow + ring_slot(sp, j);
+    const int ii = sp.ia0 + (j - sp.n_ring) * sp.ias;
+    const uint8_t *pa = ring ? sp.rA + (size_t)ri * es : (const uint8_t *)sp.iA + (size_t)ii * es;
     R.a = BF ? bf16f(*(const uint16_t *)pa) : *(const float *)pa;
     if (HASB) {
-      const uint8_t *pb = ring ? sp.rB + ri * es : (const uint8_t *)sp.iB + ii * es;
+      const uint8_t *pb = ring ? sp.rB + (size_t)ri * es : (const uint8_t *)sp.iB + (size_t)ii * es;
       R.b = BF ? bf16f(*(const uint16_t *)pb) : *(const float *)pb;
     } else {
       R.b = 0.f;
@@ -429,27 +444,37 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c0 = base + u * kThreads + t;
-    const int c = c0 < total ? c0 : total - 1;
-    const uint8_t *src;
-    int dst;
-    if (c < nV) {
-      const int j = c / cpv, e = (c - j * cpv) * epc;
-      src = j < sp.n_ring ? sp.rV + ((sp.hrow + ring_slot(sp, j)) * sp.P + e) * es
-                          : (const uint8_t *)sp.iV + (sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + e) * es;
-      dst = (int)(sp.V - lds) + j * sp.P + e;
-    } else if (c < nV + nK) {
-      const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
-      src = j < sp.n_ring ? sp.rK + ((sp.krow + ring_slot(sp, j)) * sp.N + e) * es
-                          : (const uint8_t *)sp.iK + (sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + e) * es;
-      dst = (int)(sp.K - lds) + j * (sp.N + 4) + e;
-    } else {
-      const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
-      src = (const uint8_t *)sp.iQ + (sp.iq0 + (int64_t)r * sp.iqs + e) * es;
-      dst = (int)(sp.Q - lds) + r * sp.N + e;
+    const int c = base + u * kThreads + t;
+    R.dst[u] = -1;
+    if (c < total) {                       // idle chunks skip their address arithmetic
+      const uint8_t *bp;
+      int idx, dst;
+      if (c < nV) {
+        int j;
+        if (sp.cpv_lg >= 0)
+          j = c >> sp.cpv_lg;
+        else
+          j = c / cpv;
+        const int e = (c - j * cpv) * epc;
+        const bool ring = j < sp.n_ring;
+        bp = ring ? sp.rV : (const uint8_t *)sp.iV;
+        idx = ring ? (sp.hrow + ring_slot(sp, j)) * sp.P + e : sp.iv0 + (j - sp.n_ring) * sp.ivs + e;
+        dst = (int)(sp.V - lds) + j * sp.P + e;
+      } else if (c < nV + nK) {
+        const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
+        const bool ring = j < sp.n_ring;
+        bp = ring ? sp.rK : (const uint8_t *)sp.iK;
+        idx = ring ? (sp.krow + ring_slot(sp, j)) * sp.N + e : sp.ik0 + (j - sp.n_ring) * sp.iks + e;
+        dst = (int)(sp.K - lds) + j * (sp.N + 4) + e;
+      } else {
+        const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
+        bp = (const uint8_t *)sp.iQ;
+        idx = sp.iq0 + r * sp.iqs + e;
+        dst = (int)(sp.Q - lds) + r * sp.N + e;
+      }
+      R.raw[u] = *(const uint4 *)(bp + (size_t)(uint32_t)idx * es);
+      R.dst[u] = dst;
     }
-    R.raw[u] = *(const uint4 *)src;
-    R.dst[u] = c0 < total ? dst : -1;
   }
 }
 
@@ -482,11 +507,11 @@ __device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
   for (int j = t; j < sp.nrec; j += kThreads) {
     float al, be = 0.f;
     if (j < sp.n_ring) {
-      const int64_t i = sp.hrow + ring_slot(sp, j);
+      const int i = sp.hrow + ring_slot(sp, j);
       al = ld_in(sp.rA, i, sp.bf16);
       if (sp.rB) be = ld_in(sp.rB, i, sp.bf16);
     } else {
-      const int64_t i = sp.ia0 + (int64_t)(j - sp.n_ring) * sp.ias;
+      const int i = sp.ia0 + (j - sp.n_ring) * sp.ias;
       al = ld_in(sp.iA, i, sp.bf16);
       if (sp.iB) be = ld_in(sp.iB, i, sp.bf16);
     }
@@ -496,16 +521,16 @@ __device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
   for (int e = t; e < sp.nrec * sp.P; e += kThreads) {
     const int j = e / sp.P, p = e - j * sp.P;
     sp.V[e] = j < sp.n_ring ? ld_in(sp.rV, (sp.hrow + ring_slot(sp, j)) * sp.P + p, sp.bf16)
-                            : ld_in(sp.iV, sp.iv0 + (int64_t)(j - sp.n_ring) * sp.ivs + p, sp.bf16);
+                            : ld_in(sp.iV, sp.iv0 + (j - sp.n_ring) * sp.ivs + p, sp.bf16);
   }
   for (int e = t; e < sp.nrec * sp.N; e += kThreads) {
     const int j = e / sp.N, n = e - j * sp.N;
     sp.K[j * (sp.N + 4) + n] = j < sp.n_ring ? ld_in(sp.rK, (sp.krow + ring_slot(sp, j)) * sp.N + n, sp.bf16)
-                                             : ld_in(sp.iK, sp.ik0 + (int64_t)(j - sp.n_ring) * sp.iks + n, sp.bf16);
+                                             : ld_in(sp.iK, sp.ik0 + (j - sp.n_ring) * sp.iks + n, sp.bf16);
   }
   for (int e = t; e < sp.nq * sp.N; e += kThreads) {
     const int r = e / sp.N, n = e - r * sp.N;
-    sp.Q[e] = ld_in(sp.iQ, sp.iq0 + (int64_t)r * sp.iqs + n, sp.bf16);
+    sp.Q[e] = ld_in(sp.iQ, sp.iq0 + r * sp.iqs + n, sp.bf16);
   }
 }
 
@@ -517,18 +542,19 @@ __device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L
   StageSpec sp;
   sp.nrec = n_ring + n_in;
   sp.n_ring = n_ring;
-  sp.slot0 = (int)(nk % g.C);
+  sp.slot0 = ring_mod(nk, g.C);
   sp.C = g.C;
   sp.P = g.P;
   sp.N = N;
   sp.nq = nq;
   sp.bf16 = g.bf16;
+  sp.cpv_lg = g.cpv_lg;
   sp.rA = a.ring + g.off_alpha;
   sp.rB = KIND == RSSM_KIND_GDN ? a.ring + g.off_beta : nullptr;
   sp.rV = a.ring + g.off_v;
   sp.rK = a.ring + g.off_k;
-  sp.hrow = (int64_t)(b * g.H + hh) * g.C;
-  sp.krow = (int64_t)(b * g.G + gq) * g.C;
+  sp.hrow = (b * g.H + hh) * g.C;
+  sp.krow = (b * g.G + gq) * g.C;
   sp.iA = a.alpha;
   sp.iB = KIND == RSSM_KIND_GDN ? a.beta : nullptr;
   sp.iV = a.v;
@@ -579,9 +605,9 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
                                 int qr, int slot, int t) {
   const Geom &g = a.g;
   const int P = g.P;
-  const int64_t hr = (int64_t)(b * g.H + hh) * g.C + slot;
+  const int hr = (b * g.H + hh) * g.C + slot;
   const bool lead = (hh % g.grp) == 0;
-  const int64_t kr = ((int64_t)(b * g.G + gq) * g.C + slot) * N;
+  const int kr = ((b * g.G + gq) * g.C + slot) * N;
   if (g.bf16) {
     uint16_t *rA = (uint16_t *)(a.ring + g.off_alpha);
     uint16_t *rV = (uint16_t *)(a.ring + g.off_v);
@@ -656,48 +682,67 @@ __device__ __forceinline__ void wave_decays(const float *alpha, int last, float 
   if (lane == 0) *gam = x;
 }
 
+// Dot product of two LDS rows of N floats by the 16 lanes of a group: lane l16 reads the
+// 16-byte pieces at 4 * l16 + 64 * i.  Every lane of the group returns the sum.
+template <int N>
+__device__ __forceinline__ float group_dot(const float *x, const float *y, int l16) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < (N + 63) / 64; ++i) {
+    const int n = 4 * l16 + 64 * i;
+    if (n < N) {
+      const float4 a = *(const float4 *)(x + n), b = *(const float4 *)(y + n);
+      acc = fmaf(a.x, b.x, acc);
+      acc = fmaf(a.y, b.y, acc);
+      acc = fmaf(a.z, b.z, acc);
+      acc = fmaf(a.w, b.w, acc);
+    }
+  }
+  return sum16(acc);
+}
+
+// q = d / n for 0 <= d < 2^10, 1 <= n <= 64: the float estimate (d + 1/2) / n is at least
+// 1/(2n) from an integer and within 2^-12 of its exact value, so its floor is exact.
+__device__ __forceinline__ int small_div(int d, float inv_n) { return (int)(((float)d + 0.5f) * inv_n); }
+
 // Dot products k_j . q_tau for j < nrec, tau < T, by groups of 16 lanes -> coef[tau * cap + j].
 template <int N>
 __device__ void kq_dots(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
   const int g16 = t >> 4, l16 = t & 15;
+  const float inv = 1.0f / (float)nrec;
   for (int d = g16; d < T * nrec; d += kThreads / 16) {
-    const int tau = d / nrec, j = d - tau * nrec;
-    const float *kr = lds + L.K + j * (N + 4);
-    const float *qr = lds + L.q + tau * N;
-    float acc = 0.f;
-#pragma unroll
-    for (int n = l16; n < N; n += 16) acc = fmaf(kr[n], qr[n], acc);
-    acc = sum16(acc);
+    const int tau = small_div(d, inv), j = d - tau * nrec;
+    const float acc = group_dot<N>(lds + L.K + j * (N + 4), lds + L.q + tau * N, l16);
     if (l16 == 0) lds[L.coef + tau * cap + j] = acc;
   }
 }
 
 // Gated DeltaNet: Gram matrix K^T K (i < m) and K^T q_tau for T queries over nrec records.
+// Pair p of the Gram part is (i, m) with m (m - 1) / 2 <= p < m (m + 1) / 2, i = p - m (m - 1) / 2.
 template <int N>
 __device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
   const int g16 = t >> 4, l16 = t & 15;
   const int nkq = T * nrec;
   const int nd = nkq + nrec * (nrec - 1) / 2;
+  const float inv = 1.0f / (float)nrec;
   for (int d = g16; d < nd; d += kThreads / 16) {
     const float *A, *Bv;
-    int i = 0, m = 0, tau = 0;
+    int i, m = 0, tau = 0;
     if (d < nkq) {
-      tau = d / nrec;
+      tau = small_div(d, inv);
       i = d - tau * nrec;
       A = lds + L.K + i * (N + 4);
       Bv = lds + L.q + tau * N;
     } else {
       const int pp = d - nkq;
-      m = 1;
-      while ((m * (m + 1)) / 2 <= pp) ++m;
+      m = (int)((1.f + sqrtf(8.f * (float)pp + 1.f)) * 0.5f);
+      if (m * (m - 1) / 2 > pp) --m;
+      if (m * (m + 1) / 2 <= pp) ++m;
       i = pp - (m * (m - 1)) / 2;
       A = lds + L.K + i * (N + 4);
       Bv = lds + L.K + m * (N + 4);
     }
-    float acc = 0.f;
-#pragma unroll
-    for (int n = l16; n < N; n += 16) acc = fmaf(A[n], Bv[n], acc);
-    acc = sum16(acc);
+    const float acc = group_dot<N>(A, Bv, l16);
     if (l16 == 0) {
       if (d < nkq)
         lds[L.coef + tau * cap + i] = acc;            // k_i . q_tau, replaced by e after the solve
@@ -873,9 +918,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   const bool from_copy = RC && !flush;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, 1, 1);
-  sp.ia0 = (int64_t)b * g.H + hh;
-  sp.iv0 = ((int64_t)b * g.H + hh) * P;
-  sp.ik0 = ((int64_t)b * g.G + gq) * N;
+  sp.ia0 = b * g.H + hh;
+  sp.iv0 = (b * g.H + hh) * P;
+  sp.ik0 = (b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
 
   Frag<N, RGW> F;
@@ -928,7 +973,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     else
       frag_dot(F, x, lane, part);
     write_rows<RGW>(part, lds[L.gam], lds, L, dec, lds + L.coef, nrec, P, yout, wave, lane);
-    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, nrec - 1, 0, (int)(nc % g.C), t);
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, nrec - 1, 0, ring_add(sp.slot0, hb, g.C), t);
   }
   if (t == 0) {
     a.n_committed[tile] = nc + 1;
@@ -962,12 +1007,12 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   const float *tileS = a.s + (int64_t)tile * P * N;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, T, T);
-  sp.ia0 = (int64_t)b * T * g.H + hh;
+  sp.ia0 = b * T * g.H + hh;
   sp.ias = g.H;
-  sp.iv0 = ((int64_t)b * T * g.H + hh) * P;
-  sp.ivs = (int64_t)g.H * P;
-  sp.ik0 = ((int64_t)b * T * g.G + gq) * N;
-  sp.iks = (int64_t)g.G * N;
+  sp.iv0 = (b * T * g.H + hh) * P;
+  sp.ivs = g.H * P;
+  sp.ik0 = (b * T * g.G + gq) * N;
+  sp.iks = g.G * N;
   sp.iq0 = sp.ik0;
   sp.iqs = sp.iks;
 
@@ -1006,7 +1051,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
                     hb + tau + 1, P, orow, wave, lane);
   }
   for (int tau = 0; tau < T; ++tau)
-    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, (int)((nc + tau) % g.C), t);
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), t);
 }
 
 template <int KIND, int N, int RGW>
@@ -1059,9 +1104,9 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   float *tileS = a.s + (int64_t)tile * P * N;
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, 0, 0, 1, 1);
   sp.slot0 = 0;
-  sp.ia0 = (int64_t)b * g.H + hh;
-  sp.iv0 = ((int64_t)b * g.H + hh) * P;
-  sp.ik0 = ((int64_t)b * g.G + gq) * N;
+  sp.ia0 = b * g.H + hh;
+  sp.iv0 = (b * g.H + hh) * P;
+  sp.ik0 = (b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
   Frag<N, RGW> F;
   stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });

@@ -22,6 +22,7 @@ struct Geom {
   int P, N;        // tile rows (dv) and columns (dk)
   int L, C;
   int bf16;        // inputs and ring are raw bf16 bits
+  int cpv_lg;      // log2 of the 16-byte chunks per value row, -1 if not a power of two
   int read_copy;   // RSSM_READ_*
   int64_t off_alpha, off_beta, off_v, off_k, off_q;   // byte offsets inside the ring
 };

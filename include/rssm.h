@@ -79,6 +79,9 @@ enum { RSSM_READ_NONE = 0, RSSM_READ_FP8 = 1, RSSM_READ_MXFP4 = 2 };
  *   L          flush threshold (window length; the pages use 16), L >= 1.
  *   t_max      maximum drafts per verify (1 = decode only), 1 <= t_max <= 8.
  *   capacity   ring slots C, L + t_max - 1 <= C <= 32.
+ *              Each ring region (B*H*C*dv and B*G*C*dk elements) and each step
+ *              input (B*t_max*H*dv, B*t_max*G*dk elements) holds fewer than 2^31
+ *              elements (RSSM_E_SHAPE otherwise).
  *   in_dtype   RSSM_DTYPE_F32 or RSSM_DTYPE_BF16 for alpha, beta, v, k, q and the ring.
  *   read_copy  RSSM_READ_NONE, RSSM_READ_FP8 (OCP E4M3FN codes + one fp32 scale
  *              amax/448 per 32 elements along dk) or RSSM_READ_MXFP4 (OCP MX
