@@ -915,7 +915,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   const int cap = g.C + 1;
   const LdsLayout L = lds_layout(KIND, cap, 1, P, N);
   float *tileS = a.s + (int64_t)tile * P * N;
-  const bool from_copy = RC && !flush;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, 1, 1);
   sp.ia0 = b * g.H + hh;
@@ -923,20 +922,16 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   sp.ik0 = (b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
 
-  Frag<N, RGW> F;
-  RCopy<N, RGW> RCR;
-  // the tile is streamed with nontemporal loads (read once per step; on a fold step it is
-  // written back from registers)
-  stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
-    if (from_copy)
-      readcopy_load(RCR, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
-    else
-      frag_load<N, RGW, true>(F, tileS, P, wave, lane);
-  });
-  __syncthreads();
-
-  float *yout = a.out + ((int64_t)b * g.H + hh) * P;
+  // The fold step and the output-only step stage their records separately, so the tile
+  // registers of one path are never live in the other (one shared allocation would have to
+  // hold both).  The tile is streamed with nontemporal loads (read once per step; on a fold
+  // step it is written back from registers).
+  float *yout = a.out + (b * g.H + hh) * P;
   if (flush) {
+    Frag<N, RGW> F;
+    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t,
+                                               [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+    __syncthreads();
     if (KIND == RSSM_KIND_MAMBA2) {
       if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
       __syncthreads();
@@ -950,6 +945,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
     frag_dot(F, lds + L.q, lane, part);
     write_row_sums<RGW>(part, P, yout, wave, lane);
   } else {
+    Frag<N, RGW> F;
+    RCopy<N, RGW> RCR;
+    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+      if (RC)
+        readcopy_load(RCR, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
+      else
+        frag_load<N, RGW, true>(F, tileS, P, wave, lane);
+    });
+    __syncthreads();
     const float *x;
     const float *dec = nullptr;
     if (KIND == RSSM_KIND_MAMBA2) {
@@ -968,7 +972,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       x = lds + L.r;
     }
     float part[RGW];
-    if (from_copy)
+    if (RC)
       readcopy_dot(RCR, RCF, x, lane, part);
     else
       frag_dot(F, x, lane, part);
