@@ -15,6 +15,7 @@ Other measurements of the path (--workload):
   m2_verify_b512    speculative verify(T=4) -> commit -> flush(16), B=512 (Mamba-2)
   gdn_verify_b256   the same loop for Gated DeltaNet, B=256
   --drift           read-copy output drift against the fp32 path over 4096 decode steps
+  --sweep-L         window length L in {4, 8, 16, 32}, flushes in lockstep and staggered
 """
 from __future__ import annotations
 
@@ -124,6 +125,8 @@ def flush_bytes(wl, hs_folded) -> dict:
 # ----------------------------------------------------------------------------- CPU baseline
 def _oracle_worker(args):
     wl, b, steps, barrier_at = args
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)                  # one BLAS thread per worker process
     from oracle import ReplayOracle
     from synth import decode_inputs, initial_state
     inps = [decode_inputs(wl, t, [b]) for t in range(steps)]
@@ -245,44 +248,61 @@ def _stream_copy_gbps(R, torch, stream, sh):
 
 # ----------------------------------------------------------------------------- decode
 def run_decode(args, wl, with_conventional=True) -> dict:
+    """Replay decode over `layers` independent layer instances, used round robin (launch n
+    steps layer n % layers), so no layer's state or read copy is still cached when it is read
+    again.  Timed: `reps` repetitions of K launches each, the median reported; then K more
+    launches with an event pair around each (per-launch durations for the roofline)."""
+    import statistics
     import torch
     from attention_decode_mamba_amd import rssm as R
     from attention_decode_mamba_amd.state import DeviceState, config_of
 
-    K, W = args.steps, args.warmup
+    K, W, layers, reps = args.steps, args.warmup, max(1, args.layers), max(1, args.reps)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    print(f"[bench] {wl.name}: generating inputs for {W + K} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: generating inputs for {W + K} steps, {layers} layer instances",
+          file=sys.stderr, flush=True)
     t0 = time.time()
     s0 = _s0_device(wl, torch)
     inputs = _gen_inputs(wl, W + K, torch)
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     cfg = config_of(wl)
-    ds = DeviceState(cfg)
-    ds.init(s0, sh)
+    states = [DeviceState(cfg) for _ in range(layers)]
+    for ds in states:
+        ds.init(s0, sh)
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    count = [0]                                   # launches so far
 
     def replay(t):
         d = inputs[t]
+        ds = states[count[0] % layers]
+        count[0] += 1
         R.rssm_decode_step(cfg, ds.st, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
                            y.data_ptr(), sh)
+
+    def phase(n):                                 # records in launch n's window after the append
+        return ((n // layers) % wl.L) + 1
 
     tm = _Timer(torch, stream)
     for t in range(W):
         replay(t)
-    # timed region: K steps bracketed by synchronisation, no events in between
-    total_ms = tm.total_ms(lambda i: replay(W + i), K)
-    # the same K launches again (same inputs; window phases continue from W + K), with an
-    # event pair around each launch: the per-launch durations of the roofline
+    rep_ms, rep_state, rep_total = [], [], []
+    for _ in range(reps):
+        n0 = count[0]
+        rep_ms.append(tm.total_ms(lambda i: replay(W + i), K))
+        hs = [phase(n0 + i) for i in range(K)]
+        rep_state.append(sum(step_bytes(wl, h)["state"] for h in hs))
+        rep_total.append(sum(step_bytes(wl, h)["total"] for h in hs))
+    med = sorted(range(reps), key=lambda r: rep_ms[r])[reps // 2]
+    total_ms, alg_state, alg_total = rep_ms[med], rep_state[med], rep_total[med]
+    n0 = count[0]
     (per,) = tm.per_launch_ms([lambda i: replay(W + i)], K)
-    assert ds.error() == 0
+    for ds in states:
+        assert ds.error() == 0
 
-    hs1 = [((W + i) % wl.L) + 1 for i in range(K)]
-    alg_total = sum(step_bytes(wl, h)["total"] for h in hs1)
-    alg_state = sum(step_bytes(wl, h)["state"] for h in hs1)
-    hs = [((W + K + i) % wl.L) + 1 for i in range(K)]
+    hs = [phase(n0 + i) for i in range(K)]
     alg_launch = sum(step_bytes(wl, h)["total"] for h in hs) / K
     kern_ms = sum(per)
     fold = [p for p, h in zip(per, hs) if h == wl.L]
@@ -305,23 +325,29 @@ def run_decode(args, wl, with_conventional=True) -> dict:
         "nonfold_step_ms": sum(nonfold) / max(len(nonfold), 1),
         "nonfold_GBps": (sum(nf_bytes) / len(nf_bytes)) / (sum(nonfold) / len(nonfold) * 1e-3) / 1e9
         if nonfold else None,
+        "timing": {"layers": layers, "reps": reps, "rep_ms_per_step": [m / K for m in rep_ms],
+                   "median_rep": med, "spread": (max(rep_ms) - min(rep_ms)) / statistics.median(rep_ms)},
     }
     if with_conventional:
-        conv = s0.clone()
+        convs = [s0.clone() for _ in range(layers)]
+        ccount = [0]
 
         def conventional(t):
             d = inputs[t]
+            conv = convs[ccount[0] % layers]
+            ccount[0] += 1
             R.rssm_decode_step_conventional(cfg, conv.data_ptr(), _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
                                             _p(d["k"]), _p(d["q"]), y.data_ptr(), sh)
 
         for t in range(W):
             conventional(t)
-        conv_ms = tm.total_ms(lambda i: conventional(W + i), K)
+        conv_ms = statistics.median(tm.total_ms(lambda i: conventional(W + i), K) for _ in range(reps))
         cb = conventional_bytes(wl)
         res["conventional"] = {"tokens_per_s": B * K / (conv_ms * 1e-3), "ms_per_step": conv_ms / K,
                                "state_GBps": cb["state"] / (conv_ms / K * 1e-3) / 1e9,
                                "total_GBps": cb["total"] / (conv_ms / K * 1e-3) / 1e9}
         res["speedup_vs_conventional"] = conv_ms / total_ms
+        del convs
     res["stream_copy_GBps"] = _stream_copy_gbps(R, torch, stream, sh)
     return res
 
@@ -349,6 +375,98 @@ def headline(args) -> dict:
                       "in_dtype": wl.in_dtype, "state_dtype": "fp32", "parallelism": "single_gpu"}}
     out.update(r)
     return out
+
+
+# ----------------------------------------------------------------------------- window sweep
+def run_sweep(args) -> dict:
+    """Window length sweep: Mamba-2 decode at the headline shape for L in {4, 8, 16, 32}
+    (ring capacity C = L), with all sequences folding on the same step (lockstep) and with
+    the windows staggered so that sequence b starts with b mod L records (about B / L
+    sequences fold on every step).  The stagger is set up through the API: L - 1 rounds of
+    verify(T=1) + commit, sequence b accepting its draft in the first b mod L rounds."""
+    import statistics
+    import numpy as np
+    import torch
+    from attention_decode_mamba_amd import rssm as R
+    from attention_decode_mamba_amd.state import DeviceState, config_of
+    from synth import get_workload
+
+    K, W, layers, reps = args.steps, args.warmup, max(1, args.layers), max(1, args.reps)
+    base = get_workload(WORKLOAD)
+    if args.batch:
+        base = base.replace(batch=args.batch)
+    B = base.batch
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    s0 = _s0_device(base, torch)
+    inputs = _gen_inputs(base, W + K, torch)
+    drafts = _gen_inputs(base, 31, torch, drafts_T=1)
+    y = torch.empty(B, base.n_heads, base.dv, device="cuda")
+    o = torch.empty(B, 1, base.n_heads, base.dv, device="cuda")
+    tm = _Timer(torch, stream)
+    rows = []
+    for L in args.sweep_windows:
+        wl = base.replace(L=L, capacity=L, t_max=1)
+        cfg = config_of(wl)
+        for mode in ("lockstep", "staggered"):
+            states = [DeviceState(cfg) for _ in range(layers)]
+            for ds in states:
+                ds.init(s0, sh)
+                if mode == "staggered":
+                    for r in range(L - 1):
+                        d = drafts[r]
+                        R.rssm_verify(cfg, ds.st, 1, _p(d["alpha"]), None, _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                                      o.data_ptr(), sh)
+                        acc = torch.from_numpy((np.arange(B) % L > r).astype(np.int32)).cuda()
+                        R.rssm_commit(cfg, ds.st, acc.data_ptr(), 1, sh)
+                        R.rssm_flush(cfg, ds.st, L, sh)
+            start = np.arange(B) % L if mode == "staggered" else np.zeros(B, np.int64)
+            count = [0]
+
+            def replay(t):
+                d = inputs[t]
+                ds = states[count[0] % layers]
+                count[0] += 1
+                R.rssm_decode_step(cfg, ds.st, _p(d["alpha"]), None, _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                                   y.data_ptr(), sh)
+
+            def launch_bytes(n):                  # algorithmic bytes of launch n, per sequence phase
+                hs = (start + n // layers) % L + 1
+                one = wl.replace(batch=1)
+                tot = st_b = 0
+                for h, c in zip(*np.unique(hs, return_counts=True)):
+                    sb = step_bytes(one, int(h))
+                    tot += c * sb["total"]
+                    st_b += c * sb["state"]
+                return tot, st_b
+
+            for t in range(W):
+                replay(t)
+            rep_ms = []
+            for _ in range(reps):
+                rep_ms.append(tm.total_ms(lambda i: replay(W + i), K))
+            n0 = count[0]
+            (per,) = tm.per_launch_ms([lambda i: replay(W + i)], K)
+            for ds in states:
+                assert ds.error() == 0
+            ms = statistics.median(rep_ms)
+            byts = [launch_bytes(n0 + i) for i in range(K)]
+            tot = sum(b_[0] for b_ in byts) / K
+            stb = sum(b_[1] for b_ in byts) / K
+            row = {"L": L, "mode": mode, "ms_per_step": ms / K, "tokens_per_s": B * K / (ms * 1e-3),
+                   "kernel_ms_per_launch": sum(per) / K, "launch_ms_min": min(per), "launch_ms_max": max(per),
+                   "algorithmic_GBps": tot / (sum(per) / K * 1e-3) / 1e9,
+                   "frac": tot / (sum(per) / K * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                   "state_bytes_per_step": stb, "total_bytes_per_step": tot}
+            print(f"[sweep] L={L} {mode}: {row['ms_per_step']:.4f} ms/step, launches "
+                  f"{row['launch_ms_min']:.3f}..{row['launch_ms_max']:.3f} ms", file=sys.stderr, flush=True)
+            rows.append(row)
+            del states
+    best = min(rows, key=lambda r: r["ms_per_step"])
+    return {"metric": "replay decode window sweep (Mamba-2, B=%d H128 P64 N128 bf16 inputs)" % B,
+            "rows": rows, "best": {"L": best["L"], "mode": best["mode"], "ms_per_step": best["ms_per_step"]},
+            "config": {"workload": base.name, "batch": B, "layers": layers, "reps": reps, "steps": K}}
 
 
 # ----------------------------------------------------------------------------- verify loop
@@ -508,13 +626,14 @@ def _read_counter_csv(path):
     return out
 
 
-def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, warmup):
+def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, warmup, layers, reps):
     """Per-launch HBM traffic of the decode and conventional kernels from two --pmc runs
     (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
     reads for the streaming copy of COPY_BYTES bytes."""
     from synth import get_workload
     wl = get_workload(WORKLOAD).replace(batch=batch)
-    res = {"kernel_source_hash": kernel_source_hash(), "batch": batch, "command": command}
+    res = {"kernel_source_hash": kernel_source_hash(), "batch": batch, "command": command,
+           "steps": steps, "warmup": warmup, "layers": layers, "reps": reps}
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
 
@@ -539,9 +658,10 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, wa
         res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
                       "write_mib_per_dispatch_min_max": [min(w) / 1024.0 * fw, max(w) / 1024.0 * fw]}
-    # every decode dispatch of the run: warmup, timed pass and per-launch pass
-    n = warmup + 2 * steps
-    hs = [(i % wl.L) + 1 for i in range(n)]
+    # every decode dispatch of the run: warmup, the timed repetitions and the per-launch pass;
+    # dispatch n steps layer n % layers
+    n = warmup + (reps + 1) * steps
+    hs = [((i // layers) % wl.L) + 1 for i in range(n)]
     alg = sum(step_bytes(wl, h)["total"] for h in hs) / n
     res["algorithmic_bytes_per_launch"] = alg
     if "replay_decode" in res:
@@ -559,11 +679,15 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--batch", type=int, default=0, help="override the batch of the headline workload")
+    ap.add_argument("--layers", type=int, default=4, help="layer instances used round robin (decode workloads)")
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions of K steps; the median is reported")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "gdn_b256", "m2_readcopy_b256", "m2_verify_b512", "gdn_verify_b256"])
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
     ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
     ap.add_argument("--drift", action="store_true", help="read-copy drift report and exit")
+    ap.add_argument("--sweep-L", action="store_true", help="window length sweep (lockstep and staggered) and exit")
+    ap.add_argument("--sweep-windows", type=int, nargs="+", default=[4, 8, 16, 32])
     ap.add_argument("--drift-steps", type=int, default=4096)
     ap.add_argument("--drift-batch", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -574,7 +698,8 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], PROFILE_SUMMARY,
-                               args.counter_command, args.batch or 256, args.steps, args.warmup)
+                               args.counter_command, args.batch or 256, args.steps, args.warmup, args.layers,
+                               args.reps)
         print(json.dumps(r, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -587,6 +712,9 @@ def main():
         return
     if args.drift:
         print(json.dumps(run_drift(args)))
+        return
+    if args.sweep_L:
+        print(json.dumps(run_sweep(args)))
         return
     if args.workload == WORKLOAD:
         res = headline(args)
