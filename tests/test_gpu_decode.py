@@ -6,11 +6,11 @@ import torch
 
 from attention_decode_mamba_amd import rssm as R
 from oracle import ReplayOracle
-from synth import decode_inputs, get_workload, initial_state
+from synth import decode_inputs, draft_inputs, get_workload, initial_state
 from synth.stream import StepSource
 
 from gpu_util import (TOL, assert_counters, decode, dev, new_state, ptr, relerr, ring_bits, stream,
-                      tile_relerr, to_dev_inputs)
+                      tile_relerr, to_dev_inputs, verify)
 from oracle_runs import cursor_run, decode_runs
 
 pytestmark = pytest.mark.gpu
@@ -79,6 +79,8 @@ SHAPES = [
     ("gdn", "bf16", 3, 4, 2, 40, 64, 6, 6),
     ("gdn", "fp32", 2, 2, 1, 128, 128, 16, 16),
     ("gdn", "bf16", 2, 2, 2, 33, 32, 3, 3),
+    ("mamba2", "bf16", 2, 3, 3, 64, 128, 32, 32),   # longest window: records staged in two rounds
+    ("gdn", "bf16", 2, 2, 1, 128, 128, 32, 32),
 ]
 
 
@@ -89,6 +91,46 @@ def test_decode_shapes_and_ragged_tails(shape):
     wl = base.replace(name="shape", batch=B, n_heads=H, n_qk_heads=G, dv=P, dk=N, in_dtype=dt, L=L,
                       t_max=1, capacity=C, read_copy="none")
     _run_small(wl, 3 * L + 3)
+
+
+@pytest.mark.parametrize("kind,L", [("mamba2", 4), ("mamba2", 16), ("gdn", 8)])
+def test_staggered_windows_decode(kind, L):
+    """Windows at different phases: sequence b first commits b mod L one-draft verifies
+    (verify(T=1) + commit(0 or 1)), so each decode step folds only the sequences whose window
+    fills on that step.  Every output, cursor and checkpoint against the oracle for 2L steps."""
+    base = get_workload("gdn_b256" if kind == "gdn" else "m2_tiny")
+    wl = base.replace(name="stagger", batch=2 * L + 1, n_heads=3 if kind == "mamba2" else 4,
+                      n_qk_heads=3 if kind == "mamba2" else 2, dv=24, dk=64, in_dtype="bf16", L=L, t_max=1,
+                      capacity=L, read_copy="none")
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, 1, wl.n_heads, wl.dv, device="cuda")
+    for r in range(L - 1):
+        dr = draft_inputs(wl, r, seqs, 1)
+        verify(ds, 1, to_dev_inputs(dr), o)
+        orc.verify(dr, 1)
+        acc = (np.arange(wl.batch) % L > r).astype(np.int32)
+        R.rssm_commit(ds.cfg, ds.st, ptr(dev(acc)), 1, stream())
+        orc.commit(acc, 1)
+        R.rssm_flush(ds.cfg, ds.st, L, stream())
+        orc.flush(L)
+    assert_counters(ds, orc.n_committed, orc.n_ckpt, "after staggering")
+    assert sorted(set((orc.n_committed - orc.n_ckpt).tolist())) == list(range(L))
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    for t in range(2 * L):
+        inp = decode_inputs(wl, t, seqs)
+        decode(ds, to_dev_inputs(inp), y)
+        yr = orc.decode(inp)
+        err = relerr(y.cpu().numpy(), yr).max()
+        assert err <= TOL, f"step {t}: output rel err {err:.3g}"
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {t}")
+        folded = orc.n_ckpt == orc.n_committed
+        assert 1 <= int(folded.sum()) <= 3           # b mod L hits each phase 2 or 3 times
+        e = tile_relerr(ds.ckpt().cpu().numpy()[folded], orc.S_ckpt[folded]).max()
+        assert e <= TOL, f"step {t}: checkpoint rel err {e:.3g}"
+    assert ds.error() == 0
 
 
 def test_conventional_comparator_small():
