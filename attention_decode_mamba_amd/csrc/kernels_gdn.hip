@@ -68,4 +68,15 @@ hipError_t launch_conventional_gdn(const Args &a, hipStream_t s) {
 #undef CALL
 }
 
+hipError_t launch_verify_snapshot_gdn(const Args &a, hipStream_t s) {
+  const size_t lds = lds_bytes(kKind, a.T, a.T, a.g.P, a.g.N);
+#define CALL(n, r)                                                                                  \
+  {                                                                                                 \
+    hipLaunchKernelGGL((k_verify_snapshot<kKind, n, r>), grid_of(a), dim3(kThreads), lds, s, a);    \
+    return hipGetLastError();                                                                       \
+  }
+  RSSM_DISPATCH(a.g.N, rgw_for(a.g.P), CALL)
+#undef CALL
+}
+
 }  // namespace rssm

@@ -23,6 +23,24 @@ __global__ __launch_bounds__(kThreads) void k_commit(Args a) {
   a.n_committed[idx] = nc + acc;
 }
 
+// Commit for the snapshot path: cur[b] <- (cur[b] + n_accept[b]) mod S.
+__global__ __launch_bounds__(kThreads) void k_commit_snapshot(Args a) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= a.g.B) return;
+  const int S = a.snap_slots;
+  const int cur = a.snap_cur[b];
+  const int acc = a.n_accept[b];
+  if (cur < 0 || cur >= S) {
+    atomicOr(a.err, RSSM_DEVERR_CURSOR);
+    return;
+  }
+  if (acc < 0 || acc > a.T) {
+    atomicOr(a.err, RSSM_DEVERR_ACCEPT_RANGE);
+    return;
+  }
+  a.snap_cur[b] = ring_add(cur, acc, S);
+}
+
 __global__ void k_clear_err(int32_t *err) {
   if (threadIdx.x == 0) *err = 0;
 }
@@ -48,6 +66,15 @@ hipError_t launch_commit(const Args &a, hipStream_t s) {
   const int n = a.g.B * a.g.H;
   hipLaunchKernelGGL(k_commit, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_commit_snapshot(const Args &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit_snapshot, dim3((unsigned)((a.g.B + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_snapshot(const Args &a, hipStream_t s) {
+  return a.g.kind == RSSM_KIND_GDN ? launch_verify_snapshot_gdn(a, s) : launch_verify_snapshot_m2(a, s);
 }
 
 hipError_t launch_clear_err(int32_t *err, hipStream_t s) {

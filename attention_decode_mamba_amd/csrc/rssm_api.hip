@@ -250,6 +250,49 @@ int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_a
   return hip_status(launch_commit(a, stream));
 }
 
+int rssm_verify_snapshot(const rssm_config *cfg, float *snap, const int32_t *cur, int32_t T, const void *alpha,
+                         const void *beta, const void *v, const void *k, const void *q, float *o, int32_t *err,
+                         hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if (!snap || !cur || !err) return RSSM_E_NULL;
+  if (!aligned(snap, 16) || !aligned(cur, 4) || !aligned(err, 4)) return RSSM_E_ALIGN;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, o))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, nullptr);
+  a.s = snap;
+  a.snap_cur = const_cast<int32_t *>(cur);
+  a.snap_slots = cfg->t_max + 1;
+  a.err = err;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = o;
+  a.T = T;
+  a.vec16 = vec16_ok(cfg, v, k, q);
+  return hip_status(launch_verify_snapshot(a, stream));
+}
+
+int rssm_commit_snapshot(const rssm_config *cfg, int32_t *cur, const int32_t *n_accept, int32_t T, int32_t *err,
+                         hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if (!cur || !n_accept || !err) return RSSM_E_NULL;
+  if (!aligned(cur, 4) || !aligned(n_accept, 4) || !aligned(err, 4)) return RSSM_E_ALIGN;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, nullptr);
+  a.snap_cur = cur;
+  a.snap_slots = cfg->t_max + 1;
+  a.err = err;
+  a.n_accept = n_accept;
+  a.T = T;
+  return hip_status(launch_commit_snapshot(a, stream));
+}
+
 int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *alpha, const void *beta,
                                   const void *v, const void *k, const void *q, float *y, hipStream_t stream) {
   int r = check_cfg(cfg);

@@ -1096,6 +1096,51 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   if (t == 0) a.n_ckpt[tile] = nc;
 }
 
+// One recurrence step on the register tile with staged record j:
+// Mamba-2 S <- a S + v k^T; Gated DeltaNet S <- a S + u k^T with u = b (v - a S k).
+template <int KIND, int N, int RGW>
+__device__ __forceinline__ void step_record(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int j, int P,
+                                            int wave, int lane) {
+  const int c = frag_col(lane);
+  const float al = lds[L.alpha + j];
+  const float *kr = lds + L.K + j * (N + 4) + c;
+  float u[RGW];
+  if (KIND == RSSM_KIND_MAMBA2) {
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      const int row = frag_row(wave, lane, i);
+      u[i] = (row < P) ? lds[L.V + j * P + row] : 0.f;
+    }
+  } else {
+    float w[RGW];
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) w[i] = 0.f;
+#pragma unroll
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f);
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      const int row = frag_row(wave, lane, i);
+      const float vr = (row < P) ? lds[L.V + j * P + row] : 0.f;
+      u[i] = lds[L.beta + j] * (vr - al * oct_sum(w[i]));
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < N / 32; ++f) {
+    const float4 kf = *(const float4 *)(kr + 32 * f);
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
+      F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
+      F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
+      F.s[i][f].w = fmaf(al, F.s[i][f].w, u[i] * kf.w);
+    }
+  }
+}
+
 template <int KIND, int N, int RGW>
 __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   extern __shared__ float lds[];
@@ -1115,48 +1160,57 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   Frag<N, RGW> F;
   stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
-  const int c = frag_col(lane);
-  const float al = lds[L.alpha];
-  const float *kr = lds + L.K + c;
-  float u[RGW];
-  if (KIND == RSSM_KIND_MAMBA2) {
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) {
-      const int row = frag_row(wave, lane, i);
-      u[i] = (row < P) ? lds[L.V + row] : 0.f;
-    }
-  } else {
-    float w[RGW];
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) w[i] = 0.f;
-#pragma unroll
-    for (int f = 0; f < N / 32; ++f) {
-      const float4 kf = *(const float4 *)(kr + 32 * f);
-#pragma unroll
-      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) {
-      const int row = frag_row(wave, lane, i);
-      const float vr = (row < P) ? lds[L.V + row] : 0.f;
-      u[i] = lds[L.beta] * (vr - al * oct_sum(w[i]));
-    }
-  }
-#pragma unroll
-  for (int f = 0; f < N / 32; ++f) {
-    const float4 kf = *(const float4 *)(kr + 32 * f);
-#pragma unroll
-    for (int i = 0; i < RGW; ++i) {
-      F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
-      F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
-      F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
-      F.s[i][f].w = fmaf(al, F.s[i][f].w, u[i] * kf.w);
-    }
-  }
+  step_record<KIND, N, RGW>(F, lds, L, 0, P, wave, lane);
   frag_store(F, tileS, P, wave, lane);
   float part[RGW];
   frag_dot(F, lds + L.q, lane, part);
-  write_row_sums<RGW>(part, P, a.out + ((int64_t)b * g.H + hh) * P, wave, lane);
+  write_row_sums<RGW>(part, P, a.out + (b * g.H + hh) * P, wave, lane);
+}
+
+// Snapshot-based speculative verify, the comparison point for k_verify: read the committed
+// state (snapshot slot cur[b]), apply the T drafts one after another, and write each
+// intermediate state to its own slot (cur[b] + 1 + tau) mod S and output from it: one state
+// read and T state writes per step.  Snapshots: fp32 [B][S][H][P][N], S = slots per sequence.
+template <int KIND, int N, int RGW>
+__global__ __launch_bounds__(kThreads) void k_verify_snapshot(Args a) {
+  extern __shared__ float lds[];
+  const Geom &g = a.g;
+  const int tile = tile_of_block(g.B * g.H);
+  const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int T = a.T, S = a.snap_slots;
+  const int cur = a.snap_cur[b];
+  if (cur < 0 || cur >= S) {
+    if (t == 0) atomicOr(a.err, RSSM_DEVERR_CURSOR);
+    return;
+  }
+  const int P = g.P;
+  const LdsLayout L = lds_layout(KIND, T, T, P, N);
+  const int64_t PN = (int64_t)P * N;
+  float *const base = a.s + ((int64_t)b * S * g.H + hh) * PN;    // slot s at base + s * H * PN
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, 0, 0, T, T);
+  sp.slot0 = 0;
+  sp.ia0 = b * T * g.H + hh;
+  sp.ias = g.H;
+  sp.iv0 = (b * T * g.H + hh) * P;
+  sp.ivs = g.H * P;
+  sp.ik0 = (b * T * g.G + gq) * N;
+  sp.iks = g.G * N;
+  sp.iq0 = sp.ik0;
+  sp.iqs = sp.iks;
+  Frag<N, RGW> F;
+  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+    frag_load<N, RGW, true>(F, base + (int64_t)cur * g.H * PN, P, wave, lane);
+  });
+  __syncthreads();
+  for (int tau = 0; tau < T; ++tau) {
+    step_record<KIND, N, RGW>(F, lds, L, tau, P, wave, lane);
+    const int s = ring_add(cur, 1 + tau, S);
+    frag_store(F, base + (int64_t)s * g.H * PN, P, wave, lane);
+    float part[RGW];
+    frag_dot(F, lds + L.q + tau * N, lane, part);
+    write_row_sums<RGW>(part, P, a.out + ((b * T + tau) * g.H + hh) * P, wave, lane);
+  }
 }
 
 template <int N, int RGW>

@@ -43,6 +43,8 @@ struct Args {
   int T;                                   // drafts (verify / commit)
   int min_records;                         // flush threshold
   int vec16;                               // rows can be staged in 16-byte chunks
+  int32_t *snap_cur;                       // snapshot path: committed slot per sequence [B]
+  int snap_slots;                          // snapshot path: slots per sequence (t_max + 1)
 };
 
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
@@ -92,6 +94,8 @@ hipError_t launch_flush(const Args &a, hipStream_t s);
 hipError_t launch_conventional(const Args &a, hipStream_t s);
 hipError_t launch_init(const Args &a, hipStream_t s);
 hipError_t launch_commit(const Args &a, hipStream_t s);
+hipError_t launch_verify_snapshot(const Args &a, hipStream_t s);
+hipError_t launch_commit_snapshot(const Args &a, hipStream_t s);
 hipError_t launch_clear_err(int32_t *err, hipStream_t s);
 hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
@@ -104,5 +108,7 @@ hipError_t launch_decode_gdn(const Args &a, hipStream_t s);
 hipError_t launch_verify_gdn(const Args &a, hipStream_t s);
 hipError_t launch_flush_gdn(const Args &a, hipStream_t s);
 hipError_t launch_conventional_gdn(const Args &a, hipStream_t s);
+hipError_t launch_verify_snapshot_m2(const Args &a, hipStream_t s);
+hipError_t launch_verify_snapshot_gdn(const Args &a, hipStream_t s);
 
 }  // namespace rssm

@@ -78,6 +78,9 @@ _SIGS = {
     "rssm_commit": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _VP, _I32, _VP]),
     "rssm_decode_step_conventional": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _VP, _VP,
                                              _VP, _VP, _VP, _VP]),
+    "rssm_verify_snapshot": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
+                                    _VP, _VP, _VP]),
+    "rssm_commit_snapshot": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _I32, _VP, _VP]),
     "rssm_get_error": (_I32, [ctypes.POINTER(rssm_state), _VP]),
     "rssm_stream_copy": (_I32, [_VP, _VP, ctypes.c_size_t, _VP]),
     "rssm_strerror": (ctypes.c_char_p, [_I32]),
@@ -174,6 +177,16 @@ def rssm_decode_step_conventional(cfg, s, alpha, beta, v, k, q, y, stream=0) -> 
     return _ck(lib().rssm_decode_step_conventional(ctypes.byref(cfg), _p(s), _p(alpha), _p(beta),
                                                    _p(v), _p(k), _p(q), _p(y), _p(stream)),
                "rssm_decode_step_conventional")
+
+
+def rssm_verify_snapshot(cfg, snap, cur, T: int, alpha, beta, v, k, q, o, err, stream=0) -> int:
+    return _ck(lib().rssm_verify_snapshot(ctypes.byref(cfg), _p(snap), _p(cur), T, _p(alpha), _p(beta), _p(v),
+                                          _p(k), _p(q), _p(o), _p(err), _p(stream)), "rssm_verify_snapshot")
+
+
+def rssm_commit_snapshot(cfg, cur, n_accept, T: int, err, stream=0) -> int:
+    return _ck(lib().rssm_commit_snapshot(ctypes.byref(cfg), _p(cur), _p(n_accept), T, _p(err), _p(stream)),
+               "rssm_commit_snapshot")
 
 
 def rssm_get_error(st, stream=0) -> int:

@@ -16,6 +16,7 @@ Other measurements of the path (--workload):
   gdn_verify_b256   the same loop for Gated DeltaNet, B=256
   --drift           read-copy output drift against the fp32 path over 4096 decode steps
   --sweep-L         window length L in {4, 8, 16, 32}, flushes in lockstep and staggered
+  --snapshot        with a verify workload: the snapshot-based speculative comparator
 """
 from __future__ import annotations
 
@@ -555,6 +556,75 @@ def run_verify(args, wl) -> dict:
     }
 
 
+def snapshot_verify_bytes(wl, T: int) -> dict:
+    """One snapshot-verify launch: per tile one state read and T state writes, T drafts read,
+    T output rows."""
+    s = _es(wl)
+    B, H, G, P, N = wl.batch, wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
+    head_rec, _ = _rec_bytes(wl)
+    state = B * H * 4 * P * N * (1 + T)
+    drafts = B * T * (H * head_rec + G * 2 * s * N)
+    return dict(state=state, total=state + drafts + B * T * H * 4 * P)
+
+
+def run_verify_snapshot(args, wl) -> dict:
+    """The snapshot-based speculative comparator: verify_snapshot(T) -> commit_snapshot(a) per
+    step, on the same drafts and acceptance counts as the replay loop."""
+    import torch
+    from attention_decode_mamba_amd import rssm as R
+    from attention_decode_mamba_amd.state import config_of
+    from synth import accept_counts
+
+    T = wl.t_max
+    K, W = args.steps, args.warmup
+    distinct = min(args.distinct, W + K)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    s0 = _s0_device(wl, torch)
+    drafts = _gen_inputs(wl, distinct, torch, drafts_T=T)
+    accept_dev = [torch.from_numpy(accept_counts(wl, s, T)).cuda() for s in range(W + K)]
+    cfg = config_of(wl)
+    snap = torch.empty(wl.batch, T + 1, wl.n_heads, wl.dv, wl.dk, device="cuda")
+    snap[:, 0] = s0
+    del s0
+    cur = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+
+    def verify(s):
+        d = drafts[s % distinct]
+        R.rssm_verify_snapshot(cfg, snap.data_ptr(), cur.data_ptr(), T, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
+                               _p(d["k"]), _p(d["q"]), o.data_ptr(), err.data_ptr(), sh)
+
+    def commit(s):
+        R.rssm_commit_snapshot(cfg, cur.data_ptr(), accept_dev[s].data_ptr(), T, err.data_ptr(), sh)
+
+    tm = _Timer(torch, stream)
+    for s in range(W):
+        verify(s)
+        commit(s)
+    total_ms = tm.total_ms(lambda i: (verify(W + i), commit(W + i)), K)
+    pv, pc = tm.per_launch_ms([lambda i: verify(W + i), lambda i: commit(W + i)], K)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    committed = int(sum(int(accept_dev[W + i].sum().item()) for i in range(K)))
+    vb = snapshot_verify_bytes(wl, T)
+    v_ach = vb["total"] / (sum(pv) / K * 1e-3) / 1e9
+    return {
+        "metric": f"snapshot-based speculative verify->commit, committed tokens/s ({wl.name}, T={T})",
+        "value": committed / (total_ms * 1e-3), "unit": "committed tokens/s",
+        "ms_per_step": total_ms / K, "steps": K, "warmup": W, "data": "synthetic",
+        "verify": {"ms": sum(pv) / K, "GBps": v_ach, "frac": v_ach / PEAK_HBM_GBPS,
+                   "bytes_per_launch": vb["total"], "state_bytes_per_launch": vb["state"]},
+        "commit": {"ms": sum(pc) / K},
+        "roofline": {"bound": "hbm", "kernel": "k_verify_snapshot", "achieved": v_ach, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": v_ach / PEAK_HBM_GBPS},
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.n_heads, "qk_heads": wl.n_qk_heads,
+                   "dv": wl.dv, "dk": wl.dk, "T": T, "snapshots_per_sequence": T + 1},
+    }
+
+
 # ----------------------------------------------------------------------------- read-copy drift
 def run_drift(args) -> dict:
     """Output drift of the fp8 / MXFP4 read copy against the fp32 path on the same inputs:
@@ -685,6 +755,8 @@ def main():
                     choices=[WORKLOAD, "gdn_b256", "m2_readcopy_b256", "m2_verify_b512", "gdn_verify_b256"])
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
     ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
+    ap.add_argument("--snapshot", action="store_true",
+                    help="verify workloads: time the snapshot-based comparator instead of the replay loop")
     ap.add_argument("--drift", action="store_true", help="read-copy drift report and exit")
     ap.add_argument("--sweep-L", action="store_true", help="window length sweep (lockstep and staggered) and exit")
     ap.add_argument("--sweep-windows", type=int, nargs="+", default=[4, 8, 16, 32])
@@ -727,7 +799,7 @@ def main():
         return
     if args.workload in ("m2_verify_b512", "gdn_verify_b256"):
         wl = get_workload("m2_verify_b512" if args.workload == "m2_verify_b512" else "gdn_b256")
-        res = run_verify(args, wl)
+        res = run_verify_snapshot(args, wl) if args.snapshot else run_verify(args, wl)
     else:
         wl = get_workload(args.workload)
         if args.workload == "m2_readcopy_b256":

@@ -212,6 +212,30 @@ int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *
                                   const void *beta, const void *v, const void *k,
                                   const void *q, float *y, hipStream_t stream);
 
+/* Snapshot-based speculative verify, the comparison point for rssm_verify (page 4
+ * "What shipped", verify paragraph: the conventional speculative path keeps a state per
+ * draft, one state read and T state writes per step).
+ *   snap   fp32 [B][t_max + 1][H][dv][dk] snapshots, caller-owned
+ *          (B * (t_max + 1) * H * dv * dk * 4 bytes); slot cur[b] of sequence b holds
+ *          its committed state (the caller writes it before the first call).
+ *   cur    int32 [B] on the device, committed slot per sequence.
+ *   T, alpha, beta, v, k, q, o as in rssm_verify.
+ *   err    int32 [1] on the device; a cur[b] outside 0..t_max sets RSSM_DEVERR_CURSOR
+ *          and leaves that sequence untouched.
+ * Reads slot cur[b], applies the T drafts one after another (the recurrence of `kind`),
+ * writes the state after draft tau to slot (cur[b] + 1 + tau) mod (t_max + 1) and
+ * outputs o[b][tau] from it.  Never writes slot cur[b].  Host errors as elsewhere. */
+int rssm_verify_snapshot(const rssm_config *cfg, float *snap, const int32_t *cur, int32_t T,
+                         const void *alpha, const void *beta, const void *v, const void *k,
+                         const void *q, float *o, int32_t *err, hipStream_t stream);
+
+/* Commit for the snapshot path: cur[b] <- (cur[b] + n_accept[b]) mod (t_max + 1), the
+ * state after the accepted prefix.  n_accept int32 [B] on the device in 0..T; an
+ * out-of-range value sets RSSM_DEVERR_ACCEPT_RANGE (a bad cur[b]: RSSM_DEVERR_CURSOR)
+ * in err and leaves that sequence untouched. */
+int rssm_commit_snapshot(const rssm_config *cfg, int32_t *cur, const int32_t *n_accept,
+                         int32_t T, int32_t *err, hipStream_t stream);
+
 /* Synchronise `stream`, return the device error word (>= 0, RSSM_DEVERR_* bits)
  * and clear it; a negative code if a HIP call fails. */
 int rssm_get_error(const rssm_state *st, hipStream_t stream);

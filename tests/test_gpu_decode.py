@@ -112,7 +112,8 @@ def test_staggered_windows_decode(kind, L):
         verify(ds, 1, to_dev_inputs(dr), o)
         orc.verify(dr, 1)
         acc = (np.arange(wl.batch) % L > r).astype(np.int32)
-        R.rssm_commit(ds.cfg, ds.st, ptr(dev(acc)), 1, stream())
+        acc_d = dev(acc)
+        R.rssm_commit(ds.cfg, ds.st, ptr(acc_d), 1, stream())
         orc.commit(acc, 1)
         R.rssm_flush(ds.cfg, ds.st, L, stream())
         orc.flush(L)

@@ -238,3 +238,67 @@ def test_serving_shape_gdn_decode_then_verify_sampled():
                 print(f"[serving gdn] verify step {s + 1}/{nv} worst rel err {worst_v:.3g}", flush=True)
     assert worst_d <= TOL and worst_v <= TOL
     assert ds.error() == 0
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_snapshot_verify_small(name, dtype):
+    """The snapshot-based speculative comparator: outputs of every draft against the oracle's
+    verify, the committed snapshot against the oracle's committed state after every commit,
+    and the committed slot untouched by verify."""
+    wl = _small(name, in_dtype=dtype)
+    T = wl.t_max
+    S_ = T + 1
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    cfg = new_state(wl, S0).cfg
+    snap = torch.zeros(wl.batch, S_, wl.n_heads, wl.dv, wl.dk, device="cuda")
+    snap[:, 0] = dev(S0)
+    cur = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(12):
+        dr = draft_inputs(wl, s, seqs, T)
+        c = cur.cpu().numpy()
+        before = torch.stack([snap[b, int(c[b])] for b in seqs]).cpu().numpy()
+        d = to_dev_inputs(dr)                     # held until the kernel has run
+        R.rssm_verify_snapshot(cfg, ptr(snap), ptr(cur), T, ptr(d["alpha"]), ptr(d.get("beta")), ptr(d["v"]),
+                               ptr(d["k"]), ptr(d["q"]), ptr(o), ptr(err), stream())
+        ref = orc.verify(dr, T)
+        e = relerr(o.cpu().numpy(), ref).max()
+        assert e <= TOL, f"step {s}: snapshot verify rel err {e:.3g}"
+        after = torch.stack([snap[b, int(c[b])] for b in seqs]).cpu().numpy()
+        assert np.array_equal(before.view(np.uint32), after.view(np.uint32))
+        acc = accept_counts(wl, s, T)
+        acc_d = dev(acc)
+        R.rssm_commit_snapshot(cfg, ptr(cur), ptr(acc_d), T, ptr(err), stream())
+        orc.commit(acc, T)
+        orc.flush(wl.L)
+        c = cur.cpu().numpy()
+        committed = torch.stack([snap[b, int(c[b])] for b in seqs]).cpu().numpy()
+        e = tile_relerr(committed, orc.S).max()
+        assert e <= TOL, f"step {s}: committed snapshot rel err {e:.3g}"
+    assert int(err.item()) == 0
+
+
+def test_snapshot_commit_errors():
+    """Out-of-range accept counts and slots set the device error word and leave the
+    sequence's committed slot unchanged."""
+    wl = _small("m2_verify_b512")
+    cfg = new_state(wl).cfg
+    T = wl.t_max
+    cur = torch.tensor([0, 1, 2, 3, 4, 0], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.tensor([1, T + 1, -1, 2, 0, 3], dtype=torch.int32, device="cuda")
+    R.rssm_commit_snapshot(cfg, ptr(cur), ptr(acc), T, ptr(err), stream())
+    torch.cuda.synchronize()
+    assert cur.cpu().tolist() == [1, 1, 2, 0, 4, 3]
+    assert int(err.item()) == R.RSSM_DEVERR_ACCEPT_RANGE
+    err.zero_()
+    cur = torch.tensor([T + 1, 0, 0, 0, 0, 0], dtype=torch.int32, device="cuda")
+    acc = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+    R.rssm_commit_snapshot(cfg, ptr(cur), ptr(acc), T, ptr(err), stream())
+    torch.cuda.synchronize()
+    assert cur.cpu().tolist()[0] == T + 1
+    assert int(err.item()) == R.RSSM_DEVERR_CURSOR
