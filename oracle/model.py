@@ -29,6 +29,11 @@ plain definition of what every output must equal) plus the integer cursor:
   Non-flush outputs are ``R_t q_t``; flush-step outputs come from S.  R never
   feeds S.
 
+* verify_tree / commit_tree: the drafts form a tree (parent indices, each parent an
+  earlier draft or the committed head).  Output tau follows tau's root-to-node path.
+  Commit takes the accepted path (a chain from the head); its records move to the
+  consecutive slots past the cursor, so the committed window stays contiguous.
+
 A contract violation (verify with ``h + T > C``, commit with ``a`` out of range)
 leaves that sequence untouched and sets the sticky error flag; its outputs are
 NaN here.
@@ -84,6 +89,7 @@ class ReplayOracle:
         }
         self._drafts = None
         self._drafts_T = 0
+        self._tree = None
         if track_state:
             if S0 is None:
                 S0 = np.zeros((nb, H, P, N), np.float32)
@@ -181,6 +187,7 @@ class ReplayOracle:
         O = np.full((nb, T, wl.n_heads, wl.dv), np.nan)
         self._drafts, self._drafts_T = drafts, T
         self._draft_ok = np.ones(nb, bool)
+        self._tree = None
         for i in range(nb):
             if self.n_committed[i] - self.n_ckpt[i] + T > wl.capacity:
                 self.err = True
@@ -208,6 +215,82 @@ class ReplayOracle:
             if self.track_state:
                 for t in range(a):
                     self.S[i], _ = step(wl.kind, self.S[i], self._rec(self._drafts, i, t))
+            self.n_committed[i] += a
+
+    # -- tree-shaped drafts -------------------------------------------------------
+    @staticmethod
+    def tree_paths(parent_row) -> Optional[list]:
+        """Root-to-node draft lists of a draft tree given as parent indices (-1: child of the
+        committed head; otherwise an earlier draft), or None if the encoding is invalid."""
+        paths = []
+        for t, p in enumerate(parent_row):
+            p = int(p)
+            if p < -1 or p >= t:
+                return None
+            paths.append(([] if p < 0 else list(paths[p])) + [t])
+        return paths
+
+    def verify_tree(self, drafts, T: int, parent: np.ndarray) -> np.ndarray:
+        """Append T tree-shaped drafts past the cursor (draft tau at slot n_committed + tau,
+        as in verify); output tau is the stepwise recurrence over the drafts on tau's
+        root-to-node path, applied to a temporary copy of S.  ``parent`` int [nb, T]."""
+        wl = self.wl
+        if not 1 <= T <= wl.t_max:
+            raise OracleError("T out of range")
+        nb = len(self.seqs)
+        O = np.full((nb, T, wl.n_heads, wl.dv), np.nan)
+        self._drafts, self._drafts_T = drafts, T
+        self._draft_ok = np.ones(nb, bool)
+        self._tree = np.asarray(parent)
+        for i in range(nb):
+            paths = self.tree_paths(self._tree[i, :T])
+            if paths is None or self.n_committed[i] - self.n_ckpt[i] + T > wl.capacity:
+                self.err = True
+                self._draft_ok[i] = False
+                continue
+            for t in range(T):
+                self._store(i, int((self.n_committed[i] + t) % wl.capacity), drafts, t)
+            if self.track_state:
+                for t in range(T):
+                    S_tmp = self.S[i].copy()
+                    for d in paths[t]:
+                        S_tmp, y = step(wl.kind, S_tmp, self._rec(drafts, i, d))
+                    O[i, t] = y
+        return O
+
+    def commit_tree(self, path: np.ndarray, accept: np.ndarray, T: int):
+        """Commit the accepted path of the last tree verify: path int [nb, T], its first
+        accept[i] entries a chain from the committed head (path[0] a root draft, each next
+        one a child of the previous).  The accepted drafts advance S in path order and their
+        records move to the consecutive slots n_committed + 0..a-1; then n_committed += a."""
+        wl = self.wl
+        if self._drafts is None or getattr(self, "_tree", None) is None:
+            raise OracleError("commit_tree without a preceding verify_tree")
+        C = wl.capacity
+        for i in range(len(self.seqs)):
+            a = int(accept[i])
+            h = self.n_committed[i] - self.n_ckpt[i]
+            ok = 0 <= a <= T and h + T <= C and self._draft_ok[i]
+            if ok:
+                prev = -1
+                for j in range(a):
+                    d = int(path[i, j])
+                    if not (0 <= d < T) or int(self._tree[i, d]) != prev:
+                        ok = False
+                        break
+                    prev = d
+            if not ok:
+                self.err = True
+                continue
+            nc = int(self.n_committed[i])
+            chosen = [int(path[i, j]) for j in range(a)]
+            if self.track_state:
+                recs = {f: self.ring[f][i].copy() for f in _FIELDS}
+                for j, d in enumerate(chosen):
+                    for f in _FIELDS:
+                        self.ring[f][i, (nc + j) % C] = recs[f][(nc + d) % C]
+                for d in chosen:
+                    self.S[i], _ = step(wl.kind, self.S[i], self._rec(self._drafts, i, d))
             self.n_committed[i] += a
 
     def flush(self, min_records: int):

@@ -12,7 +12,7 @@ from .gen import (
     initial_state,
     decode_inputs,
     draft_inputs,
-    accept_counts,
+    accept_counts, draft_tree,
     stack_decode_inputs,
     stack_draft_inputs,
 )
@@ -20,6 +20,6 @@ from .gen import (
 __all__ = [
     "WORKLOADS", "Workload", "get_workload",
     "bf16_bits_from_f32", "head_params", "initial_state",
-    "decode_inputs", "draft_inputs", "accept_counts",
+    "decode_inputs", "draft_inputs", "accept_counts", "draft_tree",
     "stack_decode_inputs", "stack_draft_inputs",
 ]

@@ -32,6 +32,7 @@ _TAG_S0 = 0x50
 _TAG_DECODE = 0x01
 _TAG_DRAFT = 0x02
 _TAG_ACCEPT = 0x03
+_TAG_TREE = 0x04
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -144,6 +145,33 @@ def draft_inputs(wl: Workload, step: int, seqs: Sequence[int], T: int):
 def accept_counts(wl: Workload, step: int, T: int) -> np.ndarray:
     """Accepted prefix length per sequence, U{0..T}, int32 [batch]."""
     return _rng(wl.seed, _TAG_ACCEPT, step).integers(0, T + 1, size=wl.batch).astype(np.int32)
+
+
+def draft_tree(wl: Workload, step: int, T: int):
+    """A random draft tree per sequence and an accepted path in it (input recipe only).
+
+    parent int32 [batch, T]: draft t's parent is uniform over the committed head (-1) and
+    the earlier drafts 0..t-1 (a random recursive tree).  path int32 [batch, T] and
+    accept int32 [batch]: a uniformly chosen draft's root-to-node path, of which a prefix
+    of uniform length 0..depth is accepted (entries past the accepted prefix are -1)."""
+    g = _rng(wl.seed, _TAG_TREE, step)
+    parent = np.empty((wl.batch, T), np.int32)
+    for t in range(T):
+        parent[:, t] = g.integers(-1, t, size=wl.batch)
+    node = g.integers(0, T, size=wl.batch)
+    path = np.full((wl.batch, T), -1, np.int32)
+    accept = np.zeros(wl.batch, np.int32)
+    for b in range(wl.batch):
+        chain = []
+        d = int(node[b])
+        while d >= 0:
+            chain.append(d)
+            d = int(parent[b, d])
+        chain.reverse()
+        a = int(g.integers(0, len(chain) + 1))
+        path[b, :a] = chain[:a]
+        accept[b] = a
+    return parent, path, accept
 
 
 def _decode_job(args):
