@@ -41,6 +41,83 @@ __global__ __launch_bounds__(kThreads) void k_commit_snapshot(Args a) {
   a.snap_cur[b] = ring_add(cur, acc, S);
 }
 
+// Tree commit: the accepted path's records move to the consecutive slots past the cursor,
+// then the cursor advances.  Two phases through LDS: every source is read before any
+// destination is written (a destination can be the source of a later path entry).  One
+// workgroup per (sequence, value head); the first value head of a key group moves k and q.
+__global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
+  extern __shared__ uint32_t buf[];
+  __shared__ int s_path[kMaxDrafts];
+  __shared__ int s_ok;
+  const Geom &g = a.g;
+  const int tile = blockIdx.x;
+  const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
+  const bool lead = (hh % g.grp) == 0;
+  const int t = threadIdx.x;
+  const int T = a.T;
+  const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
+  const int64_t hb = nc - nk;
+  if (hb < 0 || hb > g.C) {
+    if (t == 0) atomicOr(a.err, RSSM_DEVERR_CURSOR);
+    return;
+  }
+  const int acc = a.n_accept[b];
+  if (t == 0) {
+    int ok = acc >= 0 && acc <= T && hb + T <= g.C;
+    int prev = -1;
+    for (int j = 0; ok && j < acc; ++j) {
+      const int d = a.path[b * T + j];
+      if (d < 0 || d >= T || a.parent[b * T + d] != prev) {
+        ok = 0;
+      } else {
+        s_path[j] = d;
+        prev = d;
+      }
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  if (!s_ok) {
+    if (t == 0) atomicOr(a.err, RSSM_DEVERR_ACCEPT_RANGE);
+    return;
+  }
+  const int P = g.P, N = g.N, C = g.C;
+  const int es = g.bf16 ? 2 : 4;
+  const int nsc = g.kind == RSSM_KIND_GDN ? 2 : 1;          // alpha (and beta)
+  const int per = nsc + P + (lead ? 2 * N : 0);
+  const int total = acc * per;
+  const int slot0 = ring_mod(nc, C);
+  // element e of the record in ring slot `slot`
+  auto addr = [&](int e, int slot) -> uint8_t * {
+    const int hr = (b * g.H + hh) * C + slot;
+    const int kr = (b * g.G + gq) * C + slot;
+    if (e == 0) return a.ring + g.off_alpha + (size_t)hr * es;
+    if (e < nsc) return a.ring + g.off_beta + (size_t)hr * es;
+    e -= nsc;
+    if (e < P) return a.ring + g.off_v + ((size_t)hr * P + e) * es;
+    e -= P;
+    if (e < N) return a.ring + g.off_k + ((size_t)kr * N + e) * es;
+    return a.ring + g.off_q + ((size_t)kr * N + e - N) * es;
+  };
+  for (int i = t; i < total; i += kThreads) {
+    const int j = i / per, e = i - j * per;
+    if (s_path[j] == j) continue;                          // already in place
+    const uint8_t *src = addr(e, ring_add(slot0, s_path[j], C));
+    buf[i] = es == 2 ? (uint32_t) * (const uint16_t *)src : *(const uint32_t *)src;
+  }
+  __syncthreads();
+  for (int i = t; i < total; i += kThreads) {
+    const int j = i / per, e = i - j * per;
+    if (s_path[j] == j) continue;
+    uint8_t *dst = addr(e, ring_add(slot0, j, C));
+    if (es == 2)
+      *(uint16_t *)dst = (uint16_t)buf[i];
+    else
+      *(uint32_t *)dst = buf[i];
+  }
+  if (t == 0) a.n_committed[tile] = nc + acc;
+}
+
 __global__ void k_clear_err(int32_t *err) {
   if (threadIdx.x == 0) *err = 0;
 }
@@ -65,6 +142,12 @@ hipError_t launch_init(const Args &a, hipStream_t s) {
 hipError_t launch_commit(const Args &a, hipStream_t s) {
   const int n = a.g.B * a.g.H;
   hipLaunchKernelGGL(k_commit, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_tree(const Args &a, hipStream_t s) {
+  const size_t lds = (size_t)a.T * (2 + a.g.P + 2 * a.g.N) * sizeof(uint32_t);
+  hipLaunchKernelGGL(k_commit_tree, dim3((unsigned)(a.g.B * a.g.H)), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

@@ -250,6 +250,47 @@ int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_a
   return hip_status(launch_commit(a, stream));
 }
 
+int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T, const int32_t *parent,
+                     const void *alpha, const void *beta, const void *v, const void *k, const void *q, float *o,
+                     hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if (!parent) return RSSM_E_NULL;
+  if (!aligned(parent, 4)) return RSSM_E_ALIGN;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, o))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = o;
+  a.T = T;
+  a.parent = parent;
+  a.vec16 = vec16_ok(cfg, v, k, q);
+  return hip_status(launch_verify(a, stream));
+}
+
+int rssm_commit_tree(const rssm_config *cfg, const rssm_state *st, const int32_t *parent, const int32_t *path,
+                     const int32_t *n_accept, int32_t T, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if (!parent || !path || !n_accept) return RSSM_E_NULL;
+  if (!aligned(parent, 4) || !aligned(path, 4) || !aligned(n_accept, 4)) return RSSM_E_ALIGN;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.parent = parent;
+  a.path = path;
+  a.n_accept = n_accept;
+  a.T = T;
+  return hip_status(launch_commit_tree(a, stream));
+}
+
 int rssm_verify_snapshot(const rssm_config *cfg, float *snap, const int32_t *cur, int32_t T, const void *alpha,
                          const void *beta, const void *v, const void *k, const void *q, float *o, int32_t *err,
                          hipStream_t stream) {

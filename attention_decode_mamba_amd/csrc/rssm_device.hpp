@@ -670,15 +670,24 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
 }
 
 // ---------------------------------------------------------------- coefficient phases
-// Decays of one query over records 0..last (one wave, all lanes active):
-// dec[j] = prod_{j < m <= last} alpha_m for j <= last and 0 for last < j < cap;
-// *gam = prod_{m <= last} alpha_m.
+// Record j is on a query's path when j < hb (committed records) or draft j - hb is an
+// ancestor-or-self of the query (bit j - hb of anc).  The defaults put every record on
+// the path.  Off-path records act as neutral records (alpha = 1, beta = 0, no
+// coefficient), which leave the state unchanged.
+__device__ __forceinline__ bool on_path(int j, int hb, uint32_t anc) {
+  return j < hb || ((anc >> (j - hb)) & 1u);
+}
+
+// Decays of one query over the on-path records among 0..last (one wave, all lanes active):
+// dec[j] = prod of alpha_m over on-path m with j < m <= last for on-path j <= last, else 0;
+// *gam = prod of alpha_m over on-path m <= last.
 __device__ __forceinline__ void wave_decays(const float *alpha, int last, float *dec, float *gam, int cap,
-                                            int lane) {
-  float x = (lane <= last) ? alpha[lane] : 1.f;
+                                            int lane, int hb = 1 << 30, uint32_t anc = 0) {
+  const bool on = lane <= last && on_path(lane, hb, anc);
+  float x = on ? alpha[lane] : 1.f;
   x = wave_suffix_product(x, lane);
   const float nxt = __shfl_down(x, 1);
-  if (lane < cap) dec[lane] = (lane < last) ? nxt : (lane == last ? 1.f : 0.f);
+  if (lane < cap) dec[lane] = !on ? 0.f : (lane < last ? nxt : 1.f);
   if (lane == 0) *gam = x;
 }
 
@@ -755,35 +764,42 @@ __device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, i
 // Query-transform solve for one query over records 0..n-1 (one wave; n <= 64):
 // c_i = k_i . q - sum_{m > i} b_m c_m (k_i . k_m); writes c (cc row), e_i = d_i b_i c_i
 // (coef row, replacing k_i . q) with d_i = prod_{i < m < n} alpha_m, and G.
-__device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane) {
+// Off-path records (see on_path) enter with beta = 0 and alpha = 1.
+__device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
+                               int hb = 1 << 30, uint32_t anc = 0) {
   const float *alpha = lds + L.alpha;
   const float *beta = lds + L.beta;
   const float *gram = lds + L.gram;
   float *coef = lds + L.coef + tau * cap;
   float *cc = lds + L.cc + tau * cap;
+  const bool on = lane < n && on_path(lane, hb, anc);
+  const float bl = on ? beta[lane] : 0.f;
   float x = (lane < n) ? coef[lane] : 0.f;
   for (int m = n - 1; m >= 0; --m) {
     const float cm = lane_value(x, m);
-    if (lane < m) x = fmaf(-beta[m] * cm, gram[lane * (cap + 1) + m], x);
+    const float bm = lane_value(bl, m);
+    if (lane < m) x = fmaf(-bm * cm, gram[lane * (cap + 1) + m], x);
   }
-  float p = (lane < n) ? alpha[lane] : 1.f;
+  float p = on ? alpha[lane] : 1.f;
   p = wave_suffix_product(p, lane);
   const float d = __shfl_down(p, 1);
   if (lane < n) {
     cc[lane] = x;
-    coef[lane] = (lane == n - 1 ? 1.f : d) * beta[lane] * x;
+    coef[lane] = (lane == n - 1 ? 1.f : d) * bl * x;
   }
   if (lane == 0) lds[L.gam + tau] = p;
 }
 
-// r = q - sum_{i < n} b_i c_i k_i for query tau (threads stride over N).
+// r = q - sum_{i < n} b_i c_i k_i for query tau over on-path records (threads stride over N).
 template <int N>
-__device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int n, int tau, int t0, int stride) {
+__device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int n, int tau, int t0, int stride,
+                                    int hb = 1 << 30, uint32_t anc = 0) {
   const float *beta = lds + L.beta;
   const float *cc = lds + L.cc + tau * cap;
   for (int e = t0; e < N; e += stride) {
     float r = lds[L.q + tau * N + e];
-    for (int i = 0; i < n; ++i) r = fmaf(-beta[i] * cc[i], lds[L.K + i * (N + 4) + e], r);
+    for (int i = 0; i < n; ++i)
+      if (on_path(i, hb, anc)) r = fmaf(-beta[i] * cc[i], lds[L.K + i * (N + 4) + e], r);
     lds[L.r + tau * N + e] = r;
   }
 }
@@ -1020,16 +1036,43 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   sp.iq0 = sp.ik0;
   sp.iqs = sp.iks;
 
+  // Draft tree: draft tau's parent (a.parent [B][T], -1 = the committed head; without a
+  // tree, the previous draft).  Loaded with the records, resolved to ancestor masks after.
+  const int my_parent = t < T ? (a.parent ? a.parent[b * T + t] : t - 1) : 0;
   Frag<N, RGW> F;
   stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+  int *const par = (int *)(lds + L.anc) + T;
+  uint32_t *const anc = (uint32_t *)(lds + L.anc);
+  if (t < T) par[t] = my_parent;
   __syncthreads();
+  if (t < T) {                       // bit d of anc[tau]: draft d is on tau's root-to-node path
+    uint32_t m = 0;
+    int d = t;
+    while (d >= 0) {
+      m |= 1u << d;
+      const int pd = par[d];
+      if (pd < -1 || pd >= d) {
+        m = 0;                       // invalid encoding
+        break;
+      }
+      d = pd;
+    }
+    anc[t] = m;
+  }
+  __syncthreads();
+  for (int tau = 0; tau < T; ++tau)
+    if (anc[tau] == 0) {
+      if (t == 0) atomicOr(a.err, RSSM_DEVERR_TREE);
+      return;
+    }
 
   const float *xbase;
   const float *dec = nullptr;
   if (KIND == RSSM_KIND_MAMBA2) {
-    // W[j, tau] = prod_{j < m <= hb + tau} alpha_m (dec rows), G_tau (gam), k_j . q_tau (coef rows)
+    // W[j, tau] = product of alpha_m over on-path m with j < m <= hb + tau (dec rows), G_tau
+    // (gam), k_j . q_tau (coef rows)
     for (int tau = wave; tau < T; tau += kWaves)
-      wave_decays(lds + L.alpha, hb + tau, lds + L.dec + tau * cap, lds + L.gam + tau, cap, lane);
+      wave_decays(lds + L.alpha, hb + tau, lds + L.dec + tau * cap, lds + L.gam + tau, cap, lane, hb, anc[tau]);
     kq_dots<N>(lds, L, cap, nrec, T, t);
     __syncthreads();
     xbase = lds + L.q;
@@ -1037,11 +1080,11 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   } else {
     gram_and_kq<N>(lds, L, cap, nrec, T, t);
     __syncthreads();
-    for (int tau = wave; tau < T; tau += kWaves) gdn_solve_wave(lds, L, cap, hb + tau + 1, tau, lane);
+    for (int tau = wave; tau < T; tau += kWaves) gdn_solve_wave(lds, L, cap, hb + tau + 1, tau, lane, hb, anc[tau]);
     __syncthreads();
     for (int e = t; e < T * N; e += kThreads) {
       const int tau = e / N;
-      gdn_transform_query<N>(lds, L, cap, hb + tau + 1, tau, e - tau * N, N);
+      gdn_transform_query<N>(lds, L, cap, hb + tau + 1, tau, e - tau * N, N, hb, anc[tau]);
     }
     __syncthreads();
     xbase = lds + L.r;

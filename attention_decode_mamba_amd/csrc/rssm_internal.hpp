@@ -40,6 +40,8 @@ struct Args {
   float *out;                              // y [B][H][P] or O [B][T][H][P]
   const float *s0;                         // init source (may be null)
   const int32_t *n_accept;                 // commit
+  const int32_t *parent;                   // tree verify / commit: [B][T] parent draft, -1 = head
+  const int32_t *path;                     // tree commit: [B][T] accepted drafts in path order
   int T;                                   // drafts (verify / commit)
   int min_records;                         // flush threshold
   int vec16;                               // rows can be staged in 16-byte chunks
@@ -49,7 +51,7 @@ struct Args {
 
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
 struct LdsLayout {
-  int alpha, beta, dec, coef, cc, gam, misc, q, r, K, V, gram, total;
+  int alpha, beta, dec, coef, cc, gam, misc, anc, q, r, K, V, gram, total;
 };
 
 __host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
@@ -64,6 +66,7 @@ __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P,
   l.cc = o;    o += up4(T * cap);
   l.gam = o;   o += up4(T);
   l.misc = o;  o += 4;
+  l.anc = o;   o += up4(2 * T);     // verify: draft parents and ancestor masks (int32)
   l.q = o;     o += T * N;
   l.r = o;     o += T * N;
   l.K = o;     o += cap * (N + 4);
@@ -94,6 +97,7 @@ hipError_t launch_flush(const Args &a, hipStream_t s);
 hipError_t launch_conventional(const Args &a, hipStream_t s);
 hipError_t launch_init(const Args &a, hipStream_t s);
 hipError_t launch_commit(const Args &a, hipStream_t s);
+hipError_t launch_commit_tree(const Args &a, hipStream_t s);
 hipError_t launch_verify_snapshot(const Args &a, hipStream_t s);
 hipError_t launch_commit_snapshot(const Args &a, hipStream_t s);
 hipError_t launch_clear_err(int32_t *err, hipStream_t s);

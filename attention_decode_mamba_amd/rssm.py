@@ -29,6 +29,7 @@ RSSM_E_DEVICE = -7
 RSSM_DEVERR_VERIFY_CAPACITY = 1
 RSSM_DEVERR_ACCEPT_RANGE = 2
 RSSM_DEVERR_CURSOR = 4
+RSSM_DEVERR_TREE = 8
 
 RSSM_KIND_MAMBA2 = 0
 RSSM_KIND_GDN = 1
@@ -78,6 +79,10 @@ _SIGS = {
     "rssm_commit": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _VP, _I32, _VP]),
     "rssm_decode_step_conventional": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _VP, _VP,
                                              _VP, _VP, _VP, _VP]),
+    "rssm_verify_tree": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _I32, _VP,
+                                _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "rssm_commit_tree": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _VP, _VP, _VP, _I32,
+                                _VP]),
     "rssm_verify_snapshot": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
                                     _VP, _VP, _VP]),
     "rssm_commit_snapshot": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _I32, _VP, _VP]),
@@ -177,6 +182,16 @@ def rssm_decode_step_conventional(cfg, s, alpha, beta, v, k, q, y, stream=0) -> 
     return _ck(lib().rssm_decode_step_conventional(ctypes.byref(cfg), _p(s), _p(alpha), _p(beta),
                                                    _p(v), _p(k), _p(q), _p(y), _p(stream)),
                "rssm_decode_step_conventional")
+
+
+def rssm_verify_tree(cfg, st, T: int, parent, alpha, beta, v, k, q, o, stream=0) -> int:
+    return _ck(lib().rssm_verify_tree(ctypes.byref(cfg), ctypes.byref(st), T, _p(parent), _p(alpha), _p(beta),
+                                      _p(v), _p(k), _p(q), _p(o), _p(stream)), "rssm_verify_tree")
+
+
+def rssm_commit_tree(cfg, st, parent, path, n_accept, T: int, stream=0) -> int:
+    return _ck(lib().rssm_commit_tree(ctypes.byref(cfg), ctypes.byref(st), _p(parent), _p(path), _p(n_accept), T,
+                                      _p(stream)), "rssm_commit_tree")
 
 
 def rssm_verify_snapshot(cfg, snap, cur, T: int, alpha, beta, v, k, q, o, err, stream=0) -> int:

@@ -61,7 +61,9 @@ enum {
   RSSM_DEVERR_VERIFY_CAPACITY = 1, /* verify: h + T > capacity; sequence untouched */
   RSSM_DEVERR_ACCEPT_RANGE = 2,    /* commit: n_accept outside 0..T, or the verify it
                                       commits could not append (h + T > capacity) */
-  RSSM_DEVERR_CURSOR = 4           /* counters inconsistent (h < 0 or h > capacity) */
+  RSSM_DEVERR_CURSOR = 4,          /* counters inconsistent (h < 0 or h > capacity) */
+  RSSM_DEVERR_TREE = 8             /* tree verify: a parent index is not -1 or an earlier
+                                      draft; sequence untouched */
 };
 
 enum { RSSM_KIND_MAMBA2 = 0, RSSM_KIND_GDN = 1 };
@@ -203,6 +205,29 @@ int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const v
  * RSSM_DEVERR_ACCEPT_RANGE and leaves that sequence untouched. */
 int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_accept,
                 int32_t T, hipStream_t stream);
+
+/* Tree-shaped speculative verify (page 2, implementation paragraph: pointer-only rollback
+ * also matters for tree-based speculation, where the accepted drafts need not be
+ * consecutive; the replay form of page 4 "What shipped", verify paragraph).
+ * As rssm_verify, with parent int32 [B][T] on the device: draft tau's parent is -1 (the
+ * committed head) or an earlier draft.  Output tau comes from the state after the drafts
+ * on tau's root-to-node path only: drafts off that path enter the replay form as records
+ * with alpha = 1, beta = 0 and no contribution.  Drafts are appended at slots
+ * (n_committed + tau) % C as in rssm_verify.  An invalid parent sets RSSM_DEVERR_TREE
+ * and leaves the sequence untouched; h + T > C as in rssm_verify. */
+int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T,
+                     const int32_t *parent, const void *alpha, const void *beta,
+                     const void *v, const void *k, const void *q, float *o, hipStream_t stream);
+
+/* Commit for a tree verify: path int32 [B][T] holds the accepted drafts in path order,
+ * its first n_accept[b] entries a chain from the committed head (path[0] has parent -1,
+ * each next entry is a child of the previous one; parent as passed to the verify).  The
+ * accepted drafts' ring records move to slots (n_committed + i) % C, i < n_accept[b], so
+ * the committed window stays contiguous; then n_committed += n_accept[b].  A path that
+ * is not such a chain, n_accept outside 0..T, or h + T > C sets RSSM_DEVERR_ACCEPT_RANGE
+ * and leaves the sequence untouched.  Follow with rssm_flush(L) as after rssm_commit. */
+int rssm_commit_tree(const rssm_config *cfg, const rssm_state *st, const int32_t *parent,
+                     const int32_t *path, const int32_t *n_accept, int32_t T, hipStream_t stream);
 
 /* Conventional read-modify-write decode step, the comparison point (page 4 "What
  * shipped": every token loads the full state, updates it and stores it back).

@@ -6,7 +6,7 @@ import torch
 
 from attention_decode_mamba_amd import rssm as R
 from oracle import ReplayOracle
-from synth import accept_counts, decode_inputs, draft_inputs, get_workload, initial_state
+from synth import accept_counts, decode_inputs, draft_inputs, draft_tree, get_workload, initial_state
 from synth.stream import StepSource
 
 from gpu_util import (TOL, assert_counters, counters, decode, dev, new_state, ptr, relerr, ring_bits,
@@ -302,3 +302,129 @@ def test_snapshot_commit_errors():
     torch.cuda.synchronize()
     assert cur.cpu().tolist()[0] == T + 1
     assert int(err.item()) == R.RSSM_DEVERR_CURSOR
+
+
+def _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=True):
+    parent, path, a = draft_tree(wl, s, T)
+    dr = draft_inputs(wl, 300 + s, seqs, T)
+    d = to_dev_inputs(dr)
+    par_d, path_d, acc_d = dev(parent), dev(path), dev(a)
+    R.rssm_verify_tree(ds.cfg, ds.st, T, ptr(par_d), ptr(d["alpha"]), ptr(d.get("beta")), ptr(d["v"]),
+                       ptr(d["k"]), ptr(d["q"]), ptr(o), stream())
+    ref = orc.verify_tree(dr, T, parent)
+    e = relerr(o.cpu().numpy(), ref).max()
+    assert e <= TOL, f"step {s}: tree verify rel err {e:.3g}"
+    R.rssm_commit_tree(ds.cfg, ds.st, ptr(par_d), ptr(path_d), ptr(acc_d), T, stream())
+    orc.commit_tree(path, a, T)
+    _flush(ds, wl.L)
+    orc.flush(wl.L)
+    assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {s}")
+    if check_ring:
+        ring = {k: (None if v is None else ring_bits(v)) for k, v in ds.ring_arrays().items()}
+        for i, b in enumerate(seqs):
+            for slot in orc.live_slots(i):
+                assert np.array_equal(ring["alpha"][b, :, slot], orc.ring["alpha"][i, slot])
+                assert np.array_equal(ring["v"][b, :, slot], orc.ring["v"][i, slot])
+                assert np.array_equal(ring["k"][b, :, slot], orc.ring["k"][i, slot])
+                assert np.array_equal(ring["q"][b, :, slot], orc.ring["q"][i, slot])
+                if ring["beta"] is not None:
+                    assert np.array_equal(ring["beta"][b, :, slot], orc.ring["beta"][i, slot])
+    folded = orc.n_ckpt == orc.n_committed
+    if folded.any():
+        e = tile_relerr(ds.ckpt().cpu().numpy()[folded], orc.S_ckpt[folded]).max()
+        assert e <= TOL, f"step {s}: checkpoint rel err {e:.3g}"
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tree_spec_small(name, dtype):
+    """Tree-shaped drafts: verify_tree -> commit_tree(path) -> flush(L) against the oracle:
+    every output, cursor, committed (compacted) ring record and checkpoint."""
+    wl = _small(name, in_dtype=dtype)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(24):
+        _tree_step(ds, orc, wl, s, T, seqs, o)
+    assert ds.error() == 0
+
+
+def test_chain_tree_matches_linear_verify_bits():
+    """A tree in which every draft hangs off the previous one is the linear chain: the
+    outputs are bit-identical to rssm_verify's."""
+    for name in ("m2_verify_b512", "gdn_b256"):
+        wl = _small(name)
+        T = wl.t_max
+        seqs = list(range(wl.batch))
+        S0 = initial_state(wl, seqs)
+        lin, tree = new_state(wl, S0), new_state(wl, S0)
+        chain = dev(np.tile(np.arange(-1, T - 1, dtype=np.int32), (wl.batch, 1)))
+        o1 = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+        o2 = torch.empty_like(o1)
+        for s in range(6):
+            d = to_dev_inputs(draft_inputs(wl, s, seqs, T))
+            verify(lin, T, d, o1)
+            R.rssm_verify_tree(tree.cfg, tree.st, T, ptr(chain), ptr(d["alpha"]), ptr(d.get("beta")), ptr(d["v"]),
+                               ptr(d["k"]), ptr(d["q"]), ptr(o2), stream())
+            assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+            acc_d = dev(accept_counts(wl, s, T))
+            _commit(lin, acc_d, T)
+            path = np.where(np.arange(T)[None, :] < accept_counts(wl, s, T)[:, None], np.arange(T)[None, :], -1)
+            path_d = dev(path.astype(np.int32))
+            R.rssm_commit_tree(tree.cfg, tree.st, ptr(chain), ptr(path_d), ptr(acc_d), T, stream())
+            _flush(lin, wl.L)
+            _flush(tree, wl.L)
+        assert torch.equal(lin.ckpt().view(torch.int32), tree.ckpt().view(torch.int32))
+        assert lin.error() == 0 and tree.error() == 0
+
+
+def test_tree_contract_errors():
+    """An invalid parent index sets RSSM_DEVERR_TREE and appends nothing; a path that is not
+    a chain from the head sets RSSM_DEVERR_ACCEPT_RANGE and moves nothing."""
+    wl = _small("m2_verify_b512")
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    d = to_dev_inputs(draft_inputs(wl, 0, seqs, T))
+    parent = np.tile(np.array([-1, 0, 0, 1], np.int32), (wl.batch, 1))
+    parent[1, 2] = 2
+    par_d = dev(parent)
+    ring_before = {k: (None if v is None else v.clone()) for k, v in ds.ring_arrays().items()}
+    R.rssm_verify_tree(ds.cfg, ds.st, T, ptr(par_d), ptr(d["alpha"]), None, ptr(d["v"]), ptr(d["k"]), ptr(d["q"]),
+                       ptr(o), stream())
+    assert ds.error() == R.RSSM_DEVERR_TREE
+    ring_after = ds.ring_arrays()
+    assert torch.equal(ring_before["v"][1], ring_after["v"][1])
+    good = dev(np.tile(np.array([-1, 0, 0, 1], np.int32), (wl.batch, 1)))
+    R.rssm_verify_tree(ds.cfg, ds.st, T, ptr(good), ptr(d["alpha"]), None, ptr(d["v"]), ptr(d["k"]), ptr(d["q"]),
+                       ptr(o), stream())
+    path = np.full((wl.batch, T), -1, np.int32)
+    path[0, :2] = [0, 2]
+    path[2, :2] = [1, 0]
+    path[3, :2] = [0, 3]
+    acc = np.array([2, 0, 2, 2, 0, 0], np.int32)
+    path_d, acc_d = dev(path), dev(acc)
+    R.rssm_commit_tree(ds.cfg, ds.st, ptr(good), ptr(path_d), ptr(acc_d), T, stream())
+    assert ds.error() == R.RSSM_DEVERR_ACCEPT_RANGE
+    nc, _ = counters(ds)
+    assert nc[:, 0].tolist() == [2, 0, 0, 0, 0, 0]
+
+
+def test_tree_spec_full_heads():
+    """Tree speculation at the serving head shape (H=128, P=64, N=128, bf16, C=19) for a
+    batch of 12 sequences, 40 steps: every output, cursor and checkpoint."""
+    wl = get_workload("m2_verify_b512").replace(batch=12)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(40):
+        _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=(s % 8 == 0))
+    assert ds.error() == 0
