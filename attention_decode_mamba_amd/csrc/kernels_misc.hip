@@ -41,38 +41,41 @@ __global__ __launch_bounds__(kThreads) void k_commit_snapshot(Args a) {
   a.snap_cur[b] = ring_add(cur, acc, S);
 }
 
-// Tree commit: the accepted path's records move to the consecutive slots past the cursor,
-// then the cursor advances.  Two phases through LDS: every source is read before any
-// destination is written (a destination can be the source of a later path entry).  One
-// workgroup per (sequence, value head); the first value head of a key group moves k and q.
+// Tree commit, one workgroup per sequence: the accepted path's records (every head's
+// alpha, beta, v and every key head's k, q) move to the consecutive slots past the cursor,
+// then every head's cursor replica advances.  Record i goes from offset path[i] to offset
+// i; path[i] >= i, and a destination i is the source only of an entry j with path[j] = i,
+// which needs j <= i.  So moving the records in path order reads every source before it
+// is overwritten.
 __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
-  extern __shared__ uint32_t buf[];
-  __shared__ int s_path[kMaxDrafts];
+  __shared__ int s_path[kMaxDrafts], s_par[kMaxDrafts];
   __shared__ int s_ok;
   const Geom &g = a.g;
-  const int tile = blockIdx.x;
-  const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
-  const bool lead = (hh % g.grp) == 0;
+  const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int T = a.T;
-  const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
+  const int H = g.H, G = g.G, P = g.P, N = g.N, C = g.C;
+  const int64_t nc = a.n_committed[(int64_t)b * H], nk = a.n_ckpt[(int64_t)b * H];
   const int64_t hb = nc - nk;
-  if (hb < 0 || hb > g.C) {
+  if (hb < 0 || hb > C) {
     if (t == 0) atomicOr(a.err, RSSM_DEVERR_CURSOR);
     return;
   }
   const int acc = a.n_accept[b];
+  if (t < T) {                               // the path and parent rows in one round trip
+    s_path[t] = a.path[b * T + t];
+    s_par[t] = a.parent[b * T + t];
+  }
+  __syncthreads();
   if (t == 0) {
-    int ok = acc >= 0 && acc <= T && hb + T <= g.C;
+    int ok = acc >= 0 && acc <= T && hb + T <= C;
     int prev = -1;
     for (int j = 0; ok && j < acc; ++j) {
-      const int d = a.path[b * T + j];
-      if (d < 0 || d >= T || a.parent[b * T + d] != prev) {
+      const int d = s_path[j];
+      if (d < 0 || d >= T || s_par[d] != prev)
         ok = 0;
-      } else {
-        s_path[j] = d;
+      else
         prev = d;
-      }
     }
     s_ok = ok;
   }
@@ -81,41 +84,59 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
     if (t == 0) atomicOr(a.err, RSSM_DEVERR_ACCEPT_RANGE);
     return;
   }
-  const int P = g.P, N = g.N, C = g.C;
+  // Each thread moves the same chunk positions of every record, so one thread's program
+  // order already reads a chunk's source before any later record overwrites it.
   const int es = g.bf16 ? 2 : 4;
-  const int nsc = g.kind == RSSM_KIND_GDN ? 2 : 1;          // alpha (and beta)
-  const int per = nsc + P + (lead ? 2 * N : 0);
-  const int total = acc * per;
   const int slot0 = ring_mod(nc, C);
-  // element e of the record in ring slot `slot`
-  auto addr = [&](int e, int slot) -> uint8_t * {
-    const int hr = (b * g.H + hh) * C + slot;
-    const int kr = (b * g.G + gq) * C + slot;
-    if (e == 0) return a.ring + g.off_alpha + (size_t)hr * es;
-    if (e < nsc) return a.ring + g.off_beta + (size_t)hr * es;
-    e -= nsc;
-    if (e < P) return a.ring + g.off_v + ((size_t)hr * P + e) * es;
-    e -= P;
-    if (e < N) return a.ring + g.off_k + ((size_t)kr * N + e) * es;
-    return a.ring + g.off_q + ((size_t)kr * N + e - N) * es;
-  };
-  for (int i = t; i < total; i += kThreads) {
-    const int j = i / per, e = i - j * per;
-    if (s_path[j] == j) continue;                          // already in place
-    const uint8_t *src = addr(e, ring_add(slot0, s_path[j], C));
-    buf[i] = es == 2 ? (uint32_t) * (const uint16_t *)src : *(const uint32_t *)src;
+  const bool vec = (P * es) % 16 == 0;                        // rows in 16-byte chunks
+  for (int i = 0; i < acc; ++i) {
+    if (s_path[i] == i) continue;                            // already in place (uniform)
+    const int src = ring_add(slot0, s_path[i], C), dst = ring_add(slot0, i, C);
+    // alpha (and beta) of every value head
+    for (int h = t; h < H; h += kThreads) {
+      const size_t hr = (size_t)b * H + h;
+      for (int f = 0; f < (g.kind == RSSM_KIND_GDN ? 2 : 1); ++f) {
+        const int64_t base = f == 0 ? g.off_alpha : g.off_beta;
+        if (es == 2)
+          *(uint16_t *)(a.ring + base + (hr * C + dst) * 2) = *(const uint16_t *)(a.ring + base + (hr * C + src) * 2);
+        else
+          *(uint32_t *)(a.ring + base + (hr * C + dst) * 4) = *(const uint32_t *)(a.ring + base + (hr * C + src) * 4);
+      }
+    }
+    // k and q of every key head: N * es is a multiple of 16 bytes for every dk
+    const int cpk = N * es / 16, nk2 = 2 * G * cpk;
+    for (int c = t; c < nk2; c += kThreads) {
+      const int row = c / cpk, part = c - row * cpk;          // cpk is a power of two
+      const int which = row >= G, gg = row - which * G;
+      const int64_t base = which ? g.off_q : g.off_k;
+      const size_t kr = (size_t)b * G + gg;
+      const uint8_t *ps = a.ring + base + (kr * C + src) * N * es + part * 16;
+      uint8_t *pd = a.ring + base + (kr * C + dst) * N * es + part * 16;
+      *(uint4 *)pd = *(const uint4 *)ps;
+    }
+    // v of every value head
+    if (vec) {
+      const int cpv = P * es / 16, nvc = H * cpv;
+      for (int c = t; c < nvc; c += kThreads) {
+        const int h = g.cpv_lg >= 0 ? c >> g.cpv_lg : c / cpv, part = c - h * cpv;
+        const size_t hr = (size_t)b * H + h;
+        const uint8_t *ps = a.ring + g.off_v + (hr * C + src) * P * es + part * 16;
+        uint8_t *pd = a.ring + g.off_v + (hr * C + dst) * P * es + part * 16;
+        *(uint4 *)pd = *(const uint4 *)ps;
+      }
+    } else {
+      for (int e = t; e < H * P; e += kThreads) {
+        const int h = e / P, pp = e - h * P;
+        const size_t hr = (size_t)b * H + h;
+        const size_t os = g.off_v + ((hr * C + src) * P + pp) * es, od = g.off_v + ((hr * C + dst) * P + pp) * es;
+        if (es == 2)
+          *(uint16_t *)(a.ring + od) = *(const uint16_t *)(a.ring + os);
+        else
+          *(uint32_t *)(a.ring + od) = *(const uint32_t *)(a.ring + os);
+      }
+    }
   }
-  __syncthreads();
-  for (int i = t; i < total; i += kThreads) {
-    const int j = i / per, e = i - j * per;
-    if (s_path[j] == j) continue;
-    uint8_t *dst = addr(e, ring_add(slot0, j, C));
-    if (es == 2)
-      *(uint16_t *)dst = (uint16_t)buf[i];
-    else
-      *(uint32_t *)dst = buf[i];
-  }
-  if (t == 0) a.n_committed[tile] = nc + acc;
+  for (int h = t; h < H; h += kThreads) a.n_committed[(int64_t)b * H + h] = nc + acc;
 }
 
 __global__ void k_clear_err(int32_t *err) {
@@ -146,8 +167,7 @@ hipError_t launch_commit(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_commit_tree(const Args &a, hipStream_t s) {
-  const size_t lds = (size_t)a.T * (2 + a.g.P + 2 * a.g.N) * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_commit_tree, dim3((unsigned)(a.g.B * a.g.H)), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(k_commit_tree, dim3((unsigned)a.g.B), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

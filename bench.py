@@ -17,6 +17,7 @@ Other measurements of the path (--workload):
   --drift           read-copy output drift against the fp32 path over 4096 decode steps
   --sweep-L         window length L in {4, 8, 16, 32}, flushes in lockstep and staggered
   --snapshot        with a verify workload: the snapshot-based speculative comparator
+  --tree            with a verify workload: tree-shaped drafts, accepted path committed
 """
 from __future__ import annotations
 
@@ -471,13 +472,15 @@ def run_sweep(args) -> dict:
 
 
 # ----------------------------------------------------------------------------- verify loop
-def run_verify(args, wl) -> dict:
-    """verify(T) -> commit(a) -> flush(L) per step; a ~ U{0..T} per sequence and step."""
+def run_verify(args, wl, tree=False) -> dict:
+    """verify(T) -> commit(a) -> flush(L) per step; a ~ U{0..T} per sequence and step.  With
+    tree: the drafts form a random tree per sequence (verify_tree), and a random node's
+    root-to-node path is accepted up to a random depth (commit_tree)."""
     import numpy as np
     import torch
     from attention_decode_mamba_amd import rssm as R
     from attention_decode_mamba_amd.state import DeviceState, config_of
-    from synth import accept_counts
+    from synth import accept_counts, draft_tree
 
     T = wl.t_max
     K, W = args.steps, args.warmup
@@ -488,7 +491,12 @@ def run_verify(args, wl) -> dict:
     print(f"[bench] {wl.name}: generating {distinct} distinct draft steps (cycled)", file=sys.stderr, flush=True)
     s0 = _s0_device(wl, torch)
     drafts = _gen_inputs(wl, distinct, torch, drafts_T=T)
-    accept = [accept_counts(wl, s, T) for s in range(W + K)]
+    if tree:
+        trees = [draft_tree(wl, s, T) for s in range(W + K)]
+        accept = [tr[2] for tr in trees]
+        tree_dev = [(torch.from_numpy(tr[0]).cuda(), torch.from_numpy(tr[1]).cuda()) for tr in trees]
+    else:
+        accept = [accept_counts(wl, s, T) for s in range(W + K)]
     accept_dev = [torch.from_numpy(a).cuda() for a in accept]
     cfg = config_of(wl)
     ds = DeviceState(cfg)
@@ -497,11 +505,19 @@ def run_verify(args, wl) -> dict:
 
     def verify(s):
         d = drafts[s % distinct]
-        R.rssm_verify(cfg, ds.st, T, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
-                      o.data_ptr(), sh)
+        if tree:
+            R.rssm_verify_tree(cfg, ds.st, T, tree_dev[s][0].data_ptr(), _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
+                               _p(d["k"]), _p(d["q"]), o.data_ptr(), sh)
+        else:
+            R.rssm_verify(cfg, ds.st, T, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                          o.data_ptr(), sh)
 
     def commit(s):
-        R.rssm_commit(cfg, ds.st, accept_dev[s].data_ptr(), T, sh)
+        if tree:
+            R.rssm_commit_tree(cfg, ds.st, tree_dev[s][0].data_ptr(), tree_dev[s][1].data_ptr(),
+                               accept_dev[s].data_ptr(), T, sh)
+        else:
+            R.rssm_commit(cfg, ds.st, accept_dev[s].data_ptr(), T, sh)
 
     def flush(s):
         R.rssm_flush(cfg, ds.st, wl.L, sh)
@@ -538,10 +554,12 @@ def run_verify(args, wl) -> dict:
     v_ach = sum(b["total"] for b in vb) / (sum(pv) * 1e-3) / 1e9
     f_ach = sum(b["total"] for b in fb) / (sum(pf) * 1e-3) / 1e9
     return {
-        "metric": f"speculative verify->commit->flush, committed tokens/s ({wl.name}, T={T})",
+        "metric": f"speculative {'tree ' if tree else ''}verify->commit->flush, committed tokens/s ({wl.name}, T={T})",
         "value": committed / (total_ms * 1e-3), "unit": "committed tokens/s",
         "ms_per_step": total_ms / K, "steps": K, "warmup": W, "data": "synthetic",
-        "draft_inputs": f"{distinct} distinct draft batches cycled; accepted prefix ~ U{{0..{T}}} per step",
+        "draft_inputs": (f"{distinct} distinct draft batches cycled; " +
+                         ("random recursive draft trees, a random node's path accepted to a uniform depth"
+                          if tree else f"accepted prefix ~ U{{0..{T}}} per step")),
         "mean_accept": committed / (K * wl.batch),
         "verify": {"ms": sum(pv) / K, "GBps": v_ach, "frac": v_ach / PEAK_HBM_GBPS,
                    "bytes_per_launch": sum(b["total"] for b in vb) / K},
@@ -755,6 +773,7 @@ def main():
                     choices=[WORKLOAD, "gdn_b256", "m2_readcopy_b256", "m2_verify_b512", "gdn_verify_b256"])
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
     ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
+    ap.add_argument("--tree", action="store_true", help="verify workloads: tree-shaped drafts (verify_tree/commit_tree)")
     ap.add_argument("--snapshot", action="store_true",
                     help="verify workloads: time the snapshot-based comparator instead of the replay loop")
     ap.add_argument("--drift", action="store_true", help="read-copy drift report and exit")
@@ -799,7 +818,7 @@ def main():
         return
     if args.workload in ("m2_verify_b512", "gdn_verify_b256"):
         wl = get_workload("m2_verify_b512" if args.workload == "m2_verify_b512" else "gdn_b256")
-        res = run_verify_snapshot(args, wl) if args.snapshot else run_verify(args, wl)
+        res = run_verify_snapshot(args, wl) if args.snapshot else run_verify(args, wl, tree=args.tree)
     else:
         wl = get_workload(args.workload)
         if args.workload == "m2_readcopy_b256":
