@@ -11,7 +11,7 @@ from .rssm import (
     rssm_config, rssm_state, rssm_buffer_sizes, RssmError,
     rssm_check_config, rssm_sizes, rssm_ring_offsets, rssm_init_state, rssm_decode_step,
     rssm_flush, rssm_verify, rssm_commit, rssm_decode_step_conventional, rssm_get_error,
-    rssm_verify_snapshot, rssm_commit_snapshot, rssm_verify_tree, rssm_commit_tree,
+    rssm_verify_snapshot, rssm_commit_snapshot, rssm_verify_tree, rssm_commit_tree, rssm_verify_fold,
     rssm_stream_copy, rssm_strerror, rssm_version,
 )
 
@@ -19,6 +19,6 @@ __all__ = [
     "rssm", "rssm_config", "rssm_state", "rssm_buffer_sizes", "RssmError",
     "rssm_check_config", "rssm_sizes", "rssm_ring_offsets", "rssm_init_state", "rssm_decode_step",
     "rssm_flush", "rssm_verify", "rssm_commit", "rssm_decode_step_conventional", "rssm_get_error",
-    "rssm_verify_snapshot", "rssm_commit_snapshot", "rssm_verify_tree", "rssm_commit_tree",
+    "rssm_verify_snapshot", "rssm_commit_snapshot", "rssm_verify_tree", "rssm_commit_tree", "rssm_verify_fold",
     "rssm_stream_copy", "rssm_strerror", "rssm_version",
 ]

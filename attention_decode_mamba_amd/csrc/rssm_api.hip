@@ -274,6 +274,31 @@ int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T, co
   return hip_status(launch_verify(a, stream));
 }
 
+int rssm_verify_fold(const rssm_config *cfg, const rssm_state *st, int32_t min_records, int32_t T,
+                     const int32_t *parent, const void *alpha, const void *beta, const void *v, const void *k,
+                     const void *q, float *o, hipStream_t stream) {
+  int r = check_cfg(cfg);
+  if (r) return r;
+  if ((r = check_state(cfg, st, true))) return r;
+  if (min_records < 0) return RSSM_E_RANGE;
+  if (T < 1 || T > cfg->t_max) return RSSM_E_RANGE;
+  if (parent && !aligned(parent, 4)) return RSSM_E_ALIGN;
+  if ((r = check_inputs(cfg, alpha, beta, v, k, q, o))) return r;
+  if (cfg->batch == 0) return RSSM_OK;
+  Args a = make_args(cfg, st);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.v = v;
+  a.k = k;
+  a.q = q;
+  a.out = o;
+  a.T = T;
+  a.parent = parent;
+  a.min_records = min_records > 1 ? min_records : 1;  // the fold threshold of rssm_flush
+  a.vec16 = vec16_ok(cfg, v, k, q);
+  return hip_status(launch_verify(a, stream));
+}
+
 int rssm_commit_tree(const rssm_config *cfg, const rssm_state *st, const int32_t *parent, const int32_t *path,
                      const int32_t *n_accept, int32_t T, hipStream_t stream) {
   int r = check_cfg(cfg);

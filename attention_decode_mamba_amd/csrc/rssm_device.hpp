@@ -220,11 +220,15 @@ __device__ __forceinline__ int ilog2f(float a) {
   return -149 + (31 - __clz(u & 0x7FFFFF));
 }
 
-// Quantise the tile held in registers and store the read copy (fp8 or MXFP4).
-// A 32-element block is fragment f of one row: 8 lanes x 4 values.
-template <int N, int RGW>
-__device__ void frag_store_read_copy(const Frag<N, RGW> &F, int fmt, uint8_t *__restrict__ codes,
-                                     uint8_t *__restrict__ scales, int64_t tile, int P, int wave, int lane) {
+// Quantise the tile held in registers and store the read copy (FMT: fp8 or MXFP4; nothing
+// for RSSM_READ_NONE).  A 32-element block is fragment f of one row: 8 lanes x 4 values.
+// The format is a template parameter: a kernel that writes no read copy carries no
+// quantiser code, and one that does carries only its format's.
+template <int FMT, int N, int RGW>
+__device__ __forceinline__ void frag_store_read_copy(const Frag<N, RGW> &F, uint8_t *__restrict__ codes,
+                                                     uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
+                                                     int lane) {
+  if constexpr (FMT == RSSM_READ_NONE) return;
   const int c = frag_col(lane);
   const bool lead = (lane & 7) == 0;
 #pragma unroll
@@ -236,7 +240,7 @@ __device__ void frag_store_read_copy(const Frag<N, RGW> &F, int fmt, uint8_t *__
       const float4 v = F.s[i][f];
       float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
       am = oct_max(am);
-      if (fmt == RSSM_READ_FP8) {
+      if constexpr (FMT == RSSM_READ_FP8) {
         const float sc = __fdiv_rn(am, 448.0f);
         uint32_t w = 0;
         if (sc > 0.f)
@@ -259,6 +263,17 @@ __device__ void frag_store_read_copy(const Frag<N, RGW> &F, int fmt, uint8_t *__
       }
     }
   }
+}
+
+// Read-copy store for a format known only at run time (initialisation).
+template <int N, int RGW>
+__device__ __forceinline__ void frag_store_read_copy_rt(const Frag<N, RGW> &F, int fmt, uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
+                                                        int lane) {
+  if (fmt == RSSM_READ_FP8)
+    frag_store_read_copy<RSSM_READ_FP8>(F, codes, scales, tile, P, wave, lane);
+  else if (fmt == RSSM_READ_MXFP4)
+    frag_store_read_copy<RSSM_READ_MXFP4>(F, codes, scales, tile, P, wave, lane);
 }
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -671,9 +686,9 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
 
 // ---------------------------------------------------------------- coefficient phases
 // Record j is on a query's path when j < hb (committed records) or draft j - hb is an
-// ancestor-or-self of the query (bit j - hb of anc).  The defaults put every record on
-// the path.  Off-path records act as neutral records (alpha = 1, beta = 0, no
-// coefficient), which leave the state unchanged.
+// ancestor-or-self of the query (bit j - hb of anc).  The defaults put every record on the
+// path.  Off-path records act as neutral records (alpha = 1, beta = 0, no coefficient),
+// which leave the state unchanged.
 __device__ __forceinline__ bool on_path(int j, int hb, uint32_t anc) {
   return j < hb || ((anc >> (j - hb)) & 1u);
 }
@@ -807,7 +822,7 @@ __device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int
 // ---------------------------------------------------------------- folds
 // Mamba-2 fold: S <- G S + sum_j d_j v_j k_j^T (decays in L.dec, G in L.gam).
 template <int N, int RGW>
-__device__ void fold_m2(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
+__device__ __forceinline__ void fold_m2(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
                         int lane) {
   const int c = frag_col(lane);
   const float G = lds[L.gam];
@@ -846,7 +861,7 @@ __device__ void fold_m2(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, i
 // Gated DeltaNet fold, one delta-rule update per record in registers:
 // S <- a S ; u = b (v - S k) ; S <- S + u k^T.
 template <int N, int RGW>
-__device__ void fold_gdn(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
+__device__ __forceinline__ void fold_gdn(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
                          int lane) {
   const int c = frag_col(lane);
   for (int j = 0; j < nrec; ++j) {
@@ -956,7 +971,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       fold_gdn(F, lds, L, nrec, P, wave, lane);
     }
     frag_store(F, tileS, P, wave, lane);
-    if (RC) frag_store_read_copy(F, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
+    frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
     float part[RGW];
     frag_dot(F, lds + L.q, lane, part);
     write_row_sums<RGW>(part, P, yout, wave, lane);
@@ -1001,8 +1016,16 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   }
 }
 
-template <int KIND, int N, int RGW>
-__global__ __launch_bounds__(kThreads) void k_verify(Args a) {
+// FOLD: flush fused in front of the verify (a window with at least a.min_records records is
+// folded into the checkpoint first, exactly as a flush would, read copy in format RCF
+// included, and the verify then reads only the drafts).
+// The fold adds live registers.  A Mamba-2 fold over a register tile of RGW * N <= 256
+// (RGW <= 4, N <= 128) is held to six waves per SIMD (80 registers), which it fits without
+// spilling; measured faster than the five waves it gets unbounded.
+template <int KIND, int N, int RGW, bool FOLD, int RCF>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((FOLD && KIND == RSSM_KIND_MAMBA2 && RGW * N <= 256 && RGW <= 4 && N <= 128) ? 6 : 1)))
+void k_verify(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
@@ -1016,15 +1039,18 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     return;
   }
   const int hb = (int)hb64;
+  // The window must take the T drafts next to its committed records even when it is folded
+  // first: the draft slots then never hold a record that a sibling head of the key group may
+  // still be staging for its own fold.
   if (hb + T > g.C) {
     if (t == 0) atomicOr(a.err, RSSM_DEVERR_VERIFY_CAPACITY);
     return;
   }
-  const int nrec = hb + T;
+  const bool fold = FOLD && hb >= a.min_records;
   const int P = g.P;
   const int cap = g.C;
   const LdsLayout L = lds_layout(KIND, cap, T, P, N);
-  const float *tileS = a.s + (int64_t)tile * P * N;
+  float *tileS = a.s + (int64_t)tile * P * N;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, T, T);
   sp.ia0 = b * T * g.H + hh;
@@ -1060,48 +1086,72 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     anc[t] = m;
   }
   __syncthreads();
+  if (FOLD && fold) {                // the flush part: fold the hb committed records
+    if (KIND == RSSM_KIND_MAMBA2) {
+      if (wave == 0) wave_decays(lds + L.alpha, hb - 1, lds + L.dec, lds + L.gam, cap, lane);
+      __syncthreads();
+      fold_m2(F, lds, L, hb, P, wave, lane);
+    } else {
+      fold_gdn(F, lds, L, hb, P, wave, lane);
+    }
+    frag_store(F, tileS, P, wave, lane);
+    frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
+    if (t == 0) a.n_ckpt[tile] = nc;
+    __syncthreads();                 // the decay rows are rewritten below
+  }
   for (int tau = 0; tau < T; ++tau)
     if (anc[tau] == 0) {
       if (t == 0) atomicOr(a.err, RSSM_DEVERR_TREE);
       return;
     }
+  // A folded window's records are in the checkpoint now: the verify reads record views that
+  // start past them (the drafts only).  Otherwise the views are the staged records.
+  const int r0 = fold ? hb : 0;
+  const int hv = hb - r0;              // committed records every query sees
+  LdsLayout Lv = L;
+  Lv.alpha += r0;
+  Lv.beta += r0;
+  Lv.K += r0 * (N + 4);
+  Lv.V += r0 * P;
 
   const float *xbase;
   const float *dec = nullptr;
   if (KIND == RSSM_KIND_MAMBA2) {
-    // W[j, tau] = product of alpha_m over on-path m with j < m <= hb + tau (dec rows), G_tau
+    // W[j, tau] = product of alpha_m over on-path m with j < m <= hv + tau (dec rows), G_tau
     // (gam), k_j . q_tau (coef rows)
     for (int tau = wave; tau < T; tau += kWaves)
-      wave_decays(lds + L.alpha, hb + tau, lds + L.dec + tau * cap, lds + L.gam + tau, cap, lane, hb, anc[tau]);
-    kq_dots<N>(lds, L, cap, nrec, T, t);
+      wave_decays(lds + Lv.alpha, hv + tau, lds + Lv.dec + tau * cap, lds + Lv.gam + tau, cap, lane, hv, anc[tau]);
+    kq_dots<N>(lds, Lv, cap, hv + T, T, t);
     __syncthreads();
-    xbase = lds + L.q;
-    dec = lds + L.dec;
+    xbase = lds + Lv.q;
+    dec = lds + Lv.dec;
   } else {
-    gram_and_kq<N>(lds, L, cap, nrec, T, t);
+    gram_and_kq<N>(lds, Lv, cap, hv + T, T, t);
     __syncthreads();
-    for (int tau = wave; tau < T; tau += kWaves) gdn_solve_wave(lds, L, cap, hb + tau + 1, tau, lane, hb, anc[tau]);
+    for (int tau = wave; tau < T; tau += kWaves)
+      gdn_solve_wave(lds, Lv, cap, hv + tau + 1, tau, lane, hv, anc[tau]);
     __syncthreads();
     for (int e = t; e < T * N; e += kThreads) {
       const int tau = e / N;
-      gdn_transform_query<N>(lds, L, cap, hb + tau + 1, tau, e - tau * N, N, hb, anc[tau]);
+      gdn_transform_query<N>(lds, Lv, cap, hv + tau + 1, tau, e - tau * N, N, hv, anc[tau]);
     }
     __syncthreads();
-    xbase = lds + L.r;
+    xbase = lds + Lv.r;
   }
 
   for (int tau = 0; tau < T; ++tau) {
     float part[RGW];
     frag_dot(F, xbase + tau * N, lane, part);
     float *orow = a.out + (((int64_t)b * T + tau) * g.H + hh) * P;
-    write_rows<RGW>(part, lds[L.gam + tau], lds, L, dec ? dec + tau * cap : nullptr, lds + L.coef + tau * cap,
-                    hb + tau + 1, P, orow, wave, lane);
+    write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dec ? dec + tau * cap : nullptr, lds + Lv.coef + tau * cap,
+                    hv + tau + 1, P, orow, wave, lane);
   }
+  // draft tau goes to slot (n_committed + tau) mod C
   for (int tau = 0; tau < T; ++tau)
     append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), t);
 }
 
-template <int KIND, int N, int RGW>
+template <int KIND, int N, int RGW, int RCF>
 __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -1134,8 +1184,7 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
     fold_gdn(F, lds, L, nrec, P, wave, lane);
   }
   frag_store(F, tileS, P, wave, lane);
-  if (g.read_copy != RSSM_READ_NONE)
-    frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+  frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
   if (t == 0) a.n_ckpt[tile] = nc;
 }
 
@@ -1268,8 +1317,7 @@ __global__ __launch_bounds__(kThreads) void k_init(Args a) {
   else
     frag_zero(F);
   frag_store(F, a.s + (int64_t)tile * P * N, P, wave, lane);
-  if (g.read_copy != RSSM_READ_NONE)
-    frag_store_read_copy(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
+  frag_store_read_copy_rt(F, g.read_copy, a.s_read, a.s_read_scale, tile, P, wave, lane);
   if (t == 0) {
     a.n_committed[tile] = 0;
     a.n_ckpt[tile] = 0;

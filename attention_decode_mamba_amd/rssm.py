@@ -81,6 +81,8 @@ _SIGS = {
                                              _VP, _VP, _VP, _VP]),
     "rssm_verify_tree": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _I32, _VP,
                                 _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "rssm_verify_fold": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _I32, _I32, _VP,
+                                _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "rssm_commit_tree": (_I32, [ctypes.POINTER(rssm_config), ctypes.POINTER(rssm_state), _VP, _VP, _VP, _I32,
                                 _VP]),
     "rssm_verify_snapshot": (_I32, [ctypes.POINTER(rssm_config), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
@@ -187,6 +189,11 @@ def rssm_decode_step_conventional(cfg, s, alpha, beta, v, k, q, y, stream=0) -> 
 def rssm_verify_tree(cfg, st, T: int, parent, alpha, beta, v, k, q, o, stream=0) -> int:
     return _ck(lib().rssm_verify_tree(ctypes.byref(cfg), ctypes.byref(st), T, _p(parent), _p(alpha), _p(beta),
                                       _p(v), _p(k), _p(q), _p(o), _p(stream)), "rssm_verify_tree")
+
+
+def rssm_verify_fold(cfg, st, min_records: int, T: int, parent, alpha, beta, v, k, q, o, stream=0) -> int:
+    return _ck(lib().rssm_verify_fold(ctypes.byref(cfg), ctypes.byref(st), min_records, T, _p(parent), _p(alpha),
+                                      _p(beta), _p(v), _p(k), _p(q), _p(o), _p(stream)), "rssm_verify_fold")
 
 
 def rssm_commit_tree(cfg, st, parent, path, n_accept, T: int, stream=0) -> int:

@@ -18,6 +18,7 @@ Other measurements of the path (--workload):
   --sweep-L         window length L in {4, 8, 16, 32}, flushes in lockstep and staggered
   --snapshot        with a verify workload: the snapshot-based speculative comparator
   --tree            with a verify workload: tree-shaped drafts, accepted path committed
+  --fused           with a verify workload: verify_fold(L) -> commit (the flush fused into the verify)
 """
 from __future__ import annotations
 
@@ -472,10 +473,11 @@ def run_sweep(args) -> dict:
 
 
 # ----------------------------------------------------------------------------- verify loop
-def run_verify(args, wl, tree=False) -> dict:
+def run_verify(args, wl, tree=False, fused=False) -> dict:
     """verify(T) -> commit(a) -> flush(L) per step; a ~ U{0..T} per sequence and step.  With
     tree: the drafts form a random tree per sequence (verify_tree), and a random node's
-    root-to-node path is accepted up to a random depth (commit_tree)."""
+    root-to-node path is accepted up to a random depth (commit_tree).  With fused: the flush
+    is fused into the next verify (verify_fold(L) -> commit per step)."""
     import numpy as np
     import torch
     from attention_decode_mamba_amd import rssm as R
@@ -483,6 +485,8 @@ def run_verify(args, wl, tree=False) -> dict:
     from synth import accept_counts, draft_tree
 
     T = wl.t_max
+    if fused:                               # the fused call keeps h + T <= C before its fold
+        wl = wl.replace(capacity=wl.L + 2 * T - 1)
     K, W = args.steps, args.warmup
     distinct = min(args.distinct, W + K)
     torch.cuda.set_device(0)
@@ -505,7 +509,10 @@ def run_verify(args, wl, tree=False) -> dict:
 
     def verify(s):
         d = drafts[s % distinct]
-        if tree:
+        if fused:
+            R.rssm_verify_fold(cfg, ds.st, wl.L, T, tree_dev[s][0].data_ptr() if tree else None, _p(d["alpha"]),
+                               _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]), o.data_ptr(), sh)
+        elif tree:
             R.rssm_verify_tree(cfg, ds.st, T, tree_dev[s][0].data_ptr(), _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
                                _p(d["k"]), _p(d["q"]), o.data_ptr(), sh)
         else:
@@ -520,7 +527,8 @@ def run_verify(args, wl, tree=False) -> dict:
             R.rssm_commit(cfg, ds.st, accept_dev[s].data_ptr(), T, sh)
 
     def flush(s):
-        R.rssm_flush(cfg, ds.st, wl.L, sh)
+        if not fused:
+            R.rssm_flush(cfg, ds.st, wl.L, sh)
 
     def step(s):
         verify(s)
@@ -528,14 +536,21 @@ def run_verify(args, wl, tree=False) -> dict:
         flush(s)
 
     # host-side cursor bookkeeping for the byte counts (the same integer policy as the kernels)
+    # hist[s] = (records each window holds at verify s, records of the windows folded at step s)
     h = np.zeros(wl.batch, np.int64)
     hist = []
     for s in range(W + K):
-        h_before = h.copy()
-        h = h + accept[s]
-        folded = h >= wl.L
-        hist.append((h_before, h[folded].copy()))
-        h[folded] = 0
+        if fused:                          # the fold of the last commit happens in this verify
+            folded = h >= wl.L
+            hist.append((h.copy(), h[folded].copy()))
+            h[folded] = 0
+            h = h + accept[s]
+        else:
+            h_before = h.copy()
+            h = h + accept[s]
+            folded = h >= wl.L
+            hist.append((h_before, h[folded].copy()))
+            h[folded] = 0
 
     tm = _Timer(torch, stream)
     for s in range(W):
@@ -547,14 +562,27 @@ def run_verify(args, wl, tree=False) -> dict:
     ds.init(s0, sh)
     for s in range(W):
         step(s)
-    pv, pc, pf = tm.per_launch_ms([lambda i: verify(W + i), lambda i: commit(W + i), lambda i: flush(W + i)], K)
+    if fused:
+        pv, pc = tm.per_launch_ms([lambda i: verify(W + i), lambda i: commit(W + i)], K)
+        pf = [0.0] * K
+    else:
+        pv, pc, pf = tm.per_launch_ms([lambda i: verify(W + i), lambda i: commit(W + i), lambda i: flush(W + i)], K)
     assert ds.error() == 0
     vb = [verify_bytes(wl, hist[W + i][0], T) for i in range(K)]
     fb = [flush_bytes(wl, hist[W + i][1]) for i in range(K)]
+    if fused:
+        # the verify reads each tile and the folding windows' records anyway: the fold adds
+        # the checkpoint (and read-copy) writes of the folding tiles
+        for i in range(K):
+            nf = len(hist[W + i][1]) * wl.n_heads
+            vb[i] = {k: v + nf * (4 * wl.dv * wl.dk + _copy_write_bytes(wl)) for k, v in vb[i].items()}
+            fb[i] = {"state": 0, "total": 0}
     v_ach = sum(b["total"] for b in vb) / (sum(pv) * 1e-3) / 1e9
-    f_ach = sum(b["total"] for b in fb) / (sum(pf) * 1e-3) / 1e9
+    f_ach = (sum(b["total"] for b in fb) / (sum(pf) * 1e-3) / 1e9) if not fused else None
     return {
-        "metric": f"speculative {'tree ' if tree else ''}verify->commit->flush, committed tokens/s ({wl.name}, T={T})",
+        "metric": (f"speculative {'tree ' if tree else ''}" +
+                   ("verify_fold->commit" if fused else "verify->commit->flush") +
+                   f", committed tokens/s ({wl.name}, T={T})"),
         "value": committed / (total_ms * 1e-3), "unit": "committed tokens/s",
         "ms_per_step": total_ms / K, "steps": K, "warmup": W, "data": "synthetic",
         "draft_inputs": (f"{distinct} distinct draft batches cycled; " +
@@ -564,7 +592,7 @@ def run_verify(args, wl, tree=False) -> dict:
         "verify": {"ms": sum(pv) / K, "GBps": v_ach, "frac": v_ach / PEAK_HBM_GBPS,
                    "bytes_per_launch": sum(b["total"] for b in vb) / K},
         "commit": {"ms": sum(pc) / K},
-        "flush": {"ms": sum(pf) / K, "GBps": f_ach, "frac": f_ach / PEAK_HBM_GBPS,
+        "flush": {"ms": sum(pf) / K, "GBps": f_ach, "frac": f_ach / PEAK_HBM_GBPS if f_ach else None,
                   "bytes_per_launch": sum(b["total"] for b in fb) / K,
                   "sequences_folded_per_step": sum(len(hist[W + i][1]) for i in range(K)) / K},
         "roofline": {"bound": "hbm", "kernel": "k_verify", "achieved": v_ach, "peak": PEAK_HBM_GBPS,
@@ -774,6 +802,7 @@ def main():
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
     ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
     ap.add_argument("--tree", action="store_true", help="verify workloads: tree-shaped drafts (verify_tree/commit_tree)")
+    ap.add_argument("--fused", action="store_true", help="verify workloads: flush fused into the next verify")
     ap.add_argument("--snapshot", action="store_true",
                     help="verify workloads: time the snapshot-based comparator instead of the replay loop")
     ap.add_argument("--drift", action="store_true", help="read-copy drift report and exit")
@@ -818,7 +847,8 @@ def main():
         return
     if args.workload in ("m2_verify_b512", "gdn_verify_b256"):
         wl = get_workload("m2_verify_b512" if args.workload == "m2_verify_b512" else "gdn_b256")
-        res = run_verify_snapshot(args, wl) if args.snapshot else run_verify(args, wl, tree=args.tree)
+        res = (run_verify_snapshot(args, wl) if args.snapshot
+               else run_verify(args, wl, tree=args.tree, fused=args.fused))
     else:
         wl = get_workload(args.workload)
         if args.workload == "m2_readcopy_b256":

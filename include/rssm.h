@@ -219,6 +219,21 @@ int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T,
                      const int32_t *parent, const void *alpha, const void *beta,
                      const void *v, const void *k, const void *q, float *o, hipStream_t stream);
 
+/* Flush fused in front of a verify: rssm_flush(min_records) followed by rssm_verify(T)
+ * (parent NULL) or rssm_verify_tree(T, parent), in one launch: a sequence holding at least
+ * max(min_records, 1) records is folded into its checkpoint, read copy included, from the
+ * tile the verify reads anyway, and the verify then sees an empty window.  The speculative
+ * loop becomes verify_fold(L) -> commit, the fold of one step's commit happening at the
+ * next verify (page 4 "What shipped": the fold writes the state once; the verify reads it
+ * once).  One difference from the two calls: the capacity rule h + T <= C applies to the
+ * window BEFORE the fold (the draft slots must not hold records that other heads of the
+ * key group still read for their own folds), so a loop folding at L needs
+ * C >= L + 2 T - 1.  A sequence breaking it sets RSSM_DEVERR_VERIFY_CAPACITY and is left
+ * untouched (no fold, no output).  Other errors as the two calls. */
+int rssm_verify_fold(const rssm_config *cfg, const rssm_state *st, int32_t min_records,
+                     int32_t T, const int32_t *parent, const void *alpha, const void *beta,
+                     const void *v, const void *k, const void *q, float *o, hipStream_t stream);
+
 /* Commit for a tree verify: path int32 [B][T] holds the accepted drafts in path order,
  * its first n_accept[b] entries a chain from the committed head (path[0] has parent -1,
  * each next entry is a child of the previous one; parent as passed to the verify).  The

@@ -428,3 +428,103 @@ def test_tree_spec_full_heads():
     for s in range(40):
         _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=(s % 8 == 0))
     assert ds.error() == 0
+
+
+def _fused_loop(wl, steps, tree, seed0=400):
+    """verify_fold(L) -> commit per step against the oracle's flush(L) -> verify -> commit:
+    outputs, cursors and checkpoints after every call.  Returns the number of folds of a
+    window holding L + T - 1 records (the most a window reaches between folds)."""
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    full = 0
+    for s in range(steps):
+        nk0 = orc.n_ckpt.copy()
+        hb = orc.n_committed - nk0
+        fold = hb >= wl.L
+        full += int(np.sum(hb == wl.L + T - 1))
+        dr = draft_inputs(wl, seed0 + s, seqs, T)
+        d = to_dev_inputs(dr)
+        if tree:
+            parent, path, a = draft_tree(wl, s, T)
+        else:
+            parent, a = None, np.full(wl.batch, T, np.int32) if s % 3 == 0 else accept_counts(wl, s, T)
+            path = None
+        par_d = dev(parent) if tree else None
+        R.rssm_verify_fold(ds.cfg, ds.st, wl.L, T, ptr(par_d), ptr(d["alpha"]), ptr(d.get("beta")), ptr(d["v"]),
+                           ptr(d["k"]), ptr(d["q"]), ptr(o), stream())
+        orc.flush(wl.L)
+        ref = orc.verify_tree(dr, T, parent) if tree else orc.verify(dr, T)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {s} after verify_fold")
+        e = relerr(o.cpu().numpy(), ref).reshape(wl.batch, -1).max(axis=1)
+        bad = np.flatnonzero(e > TOL)
+        assert bad.size == 0, (f"step {s}: fused verify rel err {e.max():.3g}; sequences {bad.tolist()} "
+                               f"(window {hb[bad].tolist()}, folded {fold[bad].tolist()}, "
+                               f"n_ckpt before {nk0[bad].tolist()})")
+        if fold.any():
+            e = tile_relerr(ds.ckpt().cpu().numpy()[fold], orc.S_ckpt[fold]).max()
+            assert e <= TOL, f"step {s}: checkpoint rel err {e:.3g}"
+        acc_d = dev(a)
+        if tree:
+            path_d = dev(path)
+            R.rssm_commit_tree(ds.cfg, ds.st, ptr(par_d), ptr(path_d), ptr(acc_d), T, stream())
+            orc.commit_tree(path, a, T)
+        else:
+            _commit(ds, acc_d, T)
+            orc.commit(a, T)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {s} after commit")
+    assert ds.error() == 0
+    return full
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("tree", [False, True])
+def test_verify_with_fused_flush(name, dtype, tree):
+    """The fused loop at small shapes, the ring sized C = L + 2T - 1 as the fused call needs;
+    the linear loop must fold windows at their largest (L + T - 1 records)."""
+    wl = _small(name, in_dtype=dtype)
+    wl = wl.replace(capacity=wl.L + 2 * wl.t_max - 1)
+    full = _fused_loop(wl, 30, tree)
+    if not tree:
+        assert full > 0, "no window reached L + T - 1 records before its fold"
+
+
+def test_verify_with_fused_flush_full_heads():
+    """The fused loop at the serving head shape of Gated DeltaNet (32 value heads sharing 16
+    key heads: the key records a folding head reads are shared with its sibling head)."""
+    wl = get_workload("gdn_b256").replace(batch=8)
+    wl = wl.replace(capacity=wl.L + 2 * wl.t_max - 1)
+    _fused_loop(wl, 24, tree=False)
+
+
+def test_verify_fold_capacity_rule():
+    """A window that cannot take T drafts before its fold is a capacity error, untouched."""
+    wl = _small("m2_verify_b512", in_dtype="fp32")
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    o = torch.zeros(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    full = np.full(wl.batch, T, np.int32)
+    for s in range(4):                  # 16 committed records, C = 19
+        d = to_dev_inputs(draft_inputs(wl, 500 + s, seqs, T))
+        R.rssm_verify(ds.cfg, ds.st, T, ptr(d["alpha"]), None, ptr(d["v"]), ptr(d["k"]), ptr(d["q"]), ptr(o),
+                      stream())
+        acc_d = dev(full)
+        _commit(ds, acc_d, T)
+    assert ds.error() == 0
+    nc0, nk0 = counters(ds)
+    ck0 = ds.ckpt().clone()
+    d = to_dev_inputs(draft_inputs(wl, 600, seqs, T))
+    o.zero_()
+    R.rssm_verify_fold(ds.cfg, ds.st, wl.L, T, None, ptr(d["alpha"]), None, ptr(d["v"]), ptr(d["k"]),
+                       ptr(d["q"]), ptr(o), stream())
+    assert ds.error() == R.RSSM_DEVERR_VERIFY_CAPACITY
+    nc1, nk1 = counters(ds)
+    assert np.array_equal(nc0, nc1) and np.array_equal(nk0, nk1)
+    assert torch.equal(ck0, ds.ckpt())
+    assert not o.any()
