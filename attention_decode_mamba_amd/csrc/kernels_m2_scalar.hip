@@ -1,0 +1,6 @@
+// Mamba-2 kernel instances whose records are staged element by element (rows not 16-byte aligned).
+#include "kind_launch.hpp"
+
+namespace rssm {
+template struct KindLaunch<RSSM_KIND_MAMBA2, kStageScalar>;
+}  // namespace rssm

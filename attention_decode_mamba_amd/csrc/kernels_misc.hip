@@ -176,9 +176,6 @@ hipError_t launch_commit_snapshot(const Args &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_verify_snapshot(const Args &a, hipStream_t s) {
-  return a.g.kind == RSSM_KIND_GDN ? launch_verify_snapshot_gdn(a, s) : launch_verify_snapshot_m2(a, s);
-}
 
 hipError_t launch_clear_err(int32_t *err, hipStream_t s) {
   hipLaunchKernelGGL(k_clear_err, dim3(1), dim3(64), 0, s, err);
@@ -194,17 +191,25 @@ hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const Args &a, hipStream_t s) {
-  return a.g.kind == RSSM_KIND_GDN ? launch_decode_gdn(a, s) : launch_decode_m2(a, s);
-}
-hipError_t launch_verify(const Args &a, hipStream_t s) {
-  return a.g.kind == RSSM_KIND_GDN ? launch_verify_gdn(a, s) : launch_verify_m2(a, s);
-}
-hipError_t launch_flush(const Args &a, hipStream_t s) {
-  return a.g.kind == RSSM_KIND_GDN ? launch_flush_gdn(a, s) : launch_flush_m2(a, s);
-}
-hipError_t launch_conventional(const Args &a, hipStream_t s) {
-  return a.g.kind == RSSM_KIND_GDN ? launch_conventional_gdn(a, s) : launch_conventional_m2(a, s);
-}
+// Route a launch to the instances of the state's model kind and the call's staging path.
+#define RSSM_ROUTE(FN)                                                   \
+  {                                                                      \
+    const int stg = stage_of(a);                                         \
+    if (a.g.kind == RSSM_KIND_GDN) {                                     \
+      if (stg == kStageBf16) return KindLaunch<RSSM_KIND_GDN, kStageBf16>::FN(a, s); \
+      if (stg == kStageF32) return KindLaunch<RSSM_KIND_GDN, kStageF32>::FN(a, s);   \
+      return KindLaunch<RSSM_KIND_GDN, kStageScalar>::FN(a, s);          \
+    }                                                                    \
+    if (stg == kStageBf16) return KindLaunch<RSSM_KIND_MAMBA2, kStageBf16>::FN(a, s); \
+    if (stg == kStageF32) return KindLaunch<RSSM_KIND_MAMBA2, kStageF32>::FN(a, s);   \
+    return KindLaunch<RSSM_KIND_MAMBA2, kStageScalar>::FN(a, s);         \
+  }
+
+hipError_t launch_decode(const Args &a, hipStream_t s) RSSM_ROUTE(decode)
+hipError_t launch_verify(const Args &a, hipStream_t s) RSSM_ROUTE(verify)
+hipError_t launch_flush(const Args &a, hipStream_t s) RSSM_ROUTE(flush)
+hipError_t launch_conventional(const Args &a, hipStream_t s) RSSM_ROUTE(conventional)
+hipError_t launch_verify_snapshot(const Args &a, hipStream_t s) RSSM_ROUTE(verify_snapshot)
+#undef RSSM_ROUTE
 
 }  // namespace rssm

@@ -599,17 +599,16 @@ __device__ __forceinline__ void stage_vec_with_tile(const StageSpec &sp, float *
   }
 }
 
-template <int U, bool HASB, class IssueTile>
-__device__ __forceinline__ void stage_with_tile(const Args &a, const StageSpec &sp, float *lds, int t,
-                                                IssueTile &&issue_tile) {
-  if (a.vec16) {
-    if (sp.bf16)
-      stage_vec_with_tile<U, true, HASB>(sp, lds, t, issue_tile);
-    else
-      stage_vec_with_tile<U, false, HASB>(sp, lds, t, issue_tile);
-  } else {
+// STG (kStage*) is chosen by the launcher, so a kernel carries one staging path: with
+// several, the tile registers loaded on each path meet in one merge and the fold loop that
+// follows worked on a copy of them (twice the tile's registers live at once).
+template <int U, bool HASB, int STG, class IssueTile>
+__device__ __forceinline__ void stage_with_tile(const StageSpec &sp, float *lds, int t, IssueTile &&issue_tile) {
+  if constexpr (STG == kStageScalar) {
     issue_tile();
     stage_scalar(sp, t);
+  } else {
+    stage_vec_with_tile<U, STG == kStageBf16, HASB>(sp, lds, t, issue_tile);
   }
 }
 
@@ -777,9 +776,10 @@ __device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, i
 }
 
 // Query-transform solve for one query over records 0..n-1 (one wave; n <= 64):
-// c_i = k_i . q - sum_{m > i} b_m c_m (k_i . k_m); writes c (cc row), e_i = d_i b_i c_i
+// c_i = k_i . q - sum_{m > i} b_m c_m (k_i . k_m); writes b_i c_i (cc row), e_i = d_i b_i c_i
 // (coef row, replacing k_i . q) with d_i = prod_{i < m < n} alpha_m, and G.
-// Off-path records (see on_path) enter with beta = 0 and alpha = 1.
+// Off-path records (see on_path) enter with beta = 0 and alpha = 1, so their cc and coef
+// entries are zero.
 __device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
                                int hb = 1 << 30, uint32_t anc = 0) {
   const float *alpha = lds + L.alpha;
@@ -791,30 +791,28 @@ __device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, i
   const float bl = on ? beta[lane] : 0.f;
   float x = (lane < n) ? coef[lane] : 0.f;
   for (int m = n - 1; m >= 0; --m) {
-    const float cm = lane_value(x, m);
-    const float bm = lane_value(bl, m);
-    if (lane < m) x = fmaf(-bm * cm, gram[lane * (cap + 1) + m], x);
+    const float bcm = lane_value(bl * x, m);        // b_m c_m (c_m is final at step m)
+    if (lane < m) x = fmaf(-bcm, gram[lane * (cap + 1) + m], x);
   }
   float p = on ? alpha[lane] : 1.f;
   p = wave_suffix_product(p, lane);
   const float d = __shfl_down(p, 1);
   if (lane < n) {
-    cc[lane] = x;
-    coef[lane] = (lane == n - 1 ? 1.f : d) * bl * x;
+    const float bc = bl * x;
+    cc[lane] = bc;
+    coef[lane] = (lane == n - 1 ? 1.f : d) * bc;
   }
   if (lane == 0) lds[L.gam + tau] = p;
 }
 
-// r = q - sum_{i < n} b_i c_i k_i for query tau over on-path records (threads stride over N).
+// r = q - sum_{i < n} b_i c_i k_i for query tau (threads stride over N); the cc row holds
+// b_i c_i, zero for records off the query's path.
 template <int N>
-__device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int n, int tau, int t0, int stride,
-                                    int hb = 1 << 30, uint32_t anc = 0) {
-  const float *beta = lds + L.beta;
-  const float *cc = lds + L.cc + tau * cap;
+__device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int n, int tau, int t0, int stride) {
+  const float *bc = lds + L.cc + tau * cap;
   for (int e = t0; e < N; e += stride) {
     float r = lds[L.q + tau * N + e];
-    for (int i = 0; i < n; ++i)
-      if (on_path(i, hb, anc)) r = fmaf(-beta[i] * cc[i], lds[L.K + i * (N + 4) + e], r);
+    for (int i = 0; i < n; ++i) r = fmaf(-bc[i], lds[L.K + i * (N + 4) + e], r);
     lds[L.r + tau * N + e] = r;
   }
 }
@@ -925,7 +923,7 @@ __device__ __forceinline__ void write_rows(const float (&part)[RGW], float G, co
 // U: staging chunks per thread per round (2 covers a 17-record Mamba-2 window at 64 x 128
 // in bf16 in one round).  RCF: the read-copy format (RSSM_READ_*); with a copy the kernel
 // serves non-fold steps from it.
-template <int KIND, int N, int RGW, int RCF>
+template <int KIND, int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   constexpr int U = (KIND == RSSM_KIND_GDN || RGW > 2) ? 4 : 2;
   constexpr bool RC = RCF != RSSM_READ_NONE;
@@ -960,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   float *yout = a.out + (b * g.H + hh) * P;
   if (flush) {
     Frag<N, RGW> F;
-    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t,
+    stage_with_tile<U, KIND == RSSM_KIND_GDN, STG>(sp, lds, t,
                                                [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
     __syncthreads();
     if (KIND == RSSM_KIND_MAMBA2) {
@@ -978,7 +976,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   } else {
     Frag<N, RGW> F;
     RCopy<N, RGW> RCR;
-    stage_with_tile<U, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+    stage_with_tile<U, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() {
       if (RC)
         readcopy_load(RCR, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
       else
@@ -1019,13 +1017,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
 // FOLD: flush fused in front of the verify (a window with at least a.min_records records is
 // folded into the checkpoint first, exactly as a flush would, read copy in format RCF
 // included, and the verify then reads only the drafts).
-// The fold adds live registers.  A Mamba-2 fold over a register tile of RGW * N <= 256
-// (RGW <= 4, N <= 128) is held to six waves per SIMD (80 registers), which it fits without
-// spilling; measured faster than the five waves it gets unbounded.
-template <int KIND, int N, int RGW, bool FOLD, int RCF>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((FOLD && KIND == RSSM_KIND_MAMBA2 && RGW * N <= 256 && RGW <= 4 && N <= 128) ? 6 : 1)))
-void k_verify(Args a) {
+template <int KIND, int N, int RGW, bool FOLD, int RCF, int STG>
+__global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
   const int tile = tile_of_block(g.B * g.H);
@@ -1066,7 +1059,7 @@ void k_verify(Args a) {
   // tree, the previous draft).  Loaded with the records, resolved to ancestor masks after.
   const int my_parent = t < T ? (a.parent ? a.parent[b * T + t] : t - 1) : 0;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
   int *const par = (int *)(lds + L.anc) + T;
   uint32_t *const anc = (uint32_t *)(lds + L.anc);
   if (t < T) par[t] = my_parent;
@@ -1133,7 +1126,7 @@ void k_verify(Args a) {
     __syncthreads();
     for (int e = t; e < T * N; e += kThreads) {
       const int tau = e / N;
-      gdn_transform_query<N>(lds, Lv, cap, hv + tau + 1, tau, e - tau * N, N, hv, anc[tau]);
+      gdn_transform_query<N>(lds, Lv, cap, hv + tau + 1, tau, e - tau * N, N);
     }
     __syncthreads();
     xbase = lds + Lv.r;
@@ -1151,7 +1144,7 @@ void k_verify(Args a) {
     append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), t);
 }
 
-template <int KIND, int N, int RGW, int RCF>
+template <int KIND, int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -1174,7 +1167,7 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, nrec, 0, 0);
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
   if (KIND == RSSM_KIND_MAMBA2) {
     if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
@@ -1233,7 +1226,7 @@ __device__ __forceinline__ void step_record(Frag<N, RGW> &F, const float *lds, c
   }
 }
 
-template <int KIND, int N, int RGW>
+template <int KIND, int N, int RGW, int STG>
 __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -1250,7 +1243,7 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   sp.ik0 = (b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
   step_record<KIND, N, RGW>(F, lds, L, 0, P, wave, lane);
   frag_store(F, tileS, P, wave, lane);
@@ -1263,7 +1256,7 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
 // state (snapshot slot cur[b]), apply the T drafts one after another, and write each
 // intermediate state to its own slot (cur[b] + 1 + tau) mod S and output from it: one state
 // read and T state writes per step.  Snapshots: fp32 [B][S][H][P][N], S = slots per sequence.
-template <int KIND, int N, int RGW>
+template <int KIND, int N, int RGW, int STG>
 __global__ __launch_bounds__(kThreads) void k_verify_snapshot(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -1291,7 +1284,7 @@ __global__ __launch_bounds__(kThreads) void k_verify_snapshot(Args a) {
   sp.iq0 = sp.ik0;
   sp.iqs = sp.iks;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN>(a, sp, lds, t, [&]() {
+  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() {
     frag_load<N, RGW, true>(F, base + (int64_t)cur * g.H * PN, P, wave, lane);
   });
   __syncthreads();

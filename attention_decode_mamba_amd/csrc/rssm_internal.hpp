@@ -14,6 +14,11 @@ constexpr int kWaves = 4;
 constexpr int kMaxCapacity = 32;
 constexpr int kMaxDrafts = 8;
 constexpr int kMaxLdsBytes = 64 * 1024;
+// Record staging paths (a kernel template parameter): 16-byte chunks of bf16 or fp32
+// elements, or element-wise for layouts whose rows are not 16-byte aligned.
+constexpr int kStageScalar = 0;
+constexpr int kStageBf16 = 1;
+constexpr int kStageF32 = 2;
 
 // Everything a kernel needs to address one (sequence, value-head) tile.
 struct Geom {
@@ -103,16 +108,17 @@ hipError_t launch_commit_snapshot(const Args &a, hipStream_t s);
 hipError_t launch_clear_err(int32_t *err, hipStream_t s);
 hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
-// Kind-specific launchers (defined in kernels_m2.hip / kernels_gdn.hip).
-hipError_t launch_decode_m2(const Args &a, hipStream_t s);
-hipError_t launch_verify_m2(const Args &a, hipStream_t s);
-hipError_t launch_flush_m2(const Args &a, hipStream_t s);
-hipError_t launch_conventional_m2(const Args &a, hipStream_t s);
-hipError_t launch_decode_gdn(const Args &a, hipStream_t s);
-hipError_t launch_verify_gdn(const Args &a, hipStream_t s);
-hipError_t launch_flush_gdn(const Args &a, hipStream_t s);
-hipError_t launch_conventional_gdn(const Args &a, hipStream_t s);
-hipError_t launch_verify_snapshot_m2(const Args &a, hipStream_t s);
-hipError_t launch_verify_snapshot_gdn(const Args &a, hipStream_t s);
+// Launchers of one model kind and one staging path; each (kind, path) pair is instantiated
+// in a source file of its own (kernels_<kind>_<path>.hip).
+template <int KIND, int STG>
+struct KindLaunch {
+  static hipError_t decode(const Args &a, hipStream_t s);
+  static hipError_t verify(const Args &a, hipStream_t s);
+  static hipError_t flush(const Args &a, hipStream_t s);
+  static hipError_t conventional(const Args &a, hipStream_t s);
+  static hipError_t verify_snapshot(const Args &a, hipStream_t s);
+};
+
+inline int stage_of(const Args &a) { return !a.vec16 ? kStageScalar : (a.g.bf16 ? kStageBf16 : kStageF32); }
 
 }  // namespace rssm

@@ -38,8 +38,11 @@ METRIC = "SSM decode tokens/s + effective HBM GB/s (% of peak), B=256 H128 P64 N
 WORKLOAD = "m2_decode_b256"
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_mamba2_b256_h128_p64_n128_counters.txt")
 COPY_BYTES = 1 << 30            # size of each calibration copy (read and written)
+# the sources of the headline decode kernel (Mamba-2, bf16 records staged in 16-byte chunks)
 KERNEL_SOURCES = ["attention_decode_mamba_amd/csrc/rssm_device.hpp",
-                  "attention_decode_mamba_amd/csrc/kernels_m2.hip"]
+                  "attention_decode_mamba_amd/csrc/rssm_internal.hpp",
+                  "attention_decode_mamba_amd/csrc/kind_launch.hpp",
+                  "attention_decode_mamba_amd/csrc/kernels_m2_bf16.hip"]
 
 
 def kernel_source_hash() -> str:
