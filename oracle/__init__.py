@@ -26,7 +26,7 @@ rational arithmetic, closed-form special cases, published format tables).  The
 only parts without an independent pin are listed as "parity unpinned" in the
 modules that hold them.
 """
-from .recurrence import widen, mamba2_step, gdn_step, step, expand_heads
+from .recurrence import widen, mamba2_step, gdn_step, kda_step, step, expand_heads
 from .quant import (
     e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode,
     quantize_fp8_blocks, dequantize_fp8_blocks,
@@ -37,7 +37,7 @@ from .model import ReplayOracle, OracleError
 from . import replay_forms
 
 __all__ = [
-    "widen", "mamba2_step", "gdn_step", "step", "expand_heads",
+    "widen", "mamba2_step", "gdn_step", "kda_step", "step", "expand_heads",
     "e4m3_encode", "e4m3_decode", "e2m1_encode", "e2m1_decode",
     "quantize_fp8_blocks", "dequantize_fp8_blocks",
     "quantize_mxfp4_blocks", "dequantize_mxfp4_blocks", "read_copy_dequant",

@@ -80,8 +80,10 @@ class ReplayOracle:
         H, G, P, N, C = wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk, wl.capacity
         dt = np.float32 if wl.in_dtype == "fp32" else np.uint16
         # ring of raw stored inputs (bit-exact copies of what was appended)
+        # KDA gates are per (value head, key channel); the other kinds have one per head
+        a_shape = (nb, C, H, N) if wl.kind == "kda" else (nb, C, H)
         self.ring = {
-            "alpha": np.zeros((nb, C, H), dt),
+            "alpha": np.zeros(a_shape, dt),
             "beta": np.zeros((nb, C, H), dt),
             "v": np.zeros((nb, C, H, P), dt),
             "k": np.zeros((nb, C, G, N), dt),

@@ -13,6 +13,17 @@ section; page 4, "What shipped" and "Why it matters") without a formula.  The
 reading used here is the published Gated DeltaNet rule
     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t,
 evaluated in the order: decay, error against the decayed state, rank-1 write.
+
+Kimi Delta Attention (KDA) -- page 1 (models section) and page 4 (opening
+paragraph) list KDA as the SSM layer of Kimi-K3; page 4 "Why it matters" says
+the replay reframing carries over to KDA's delta-rule update, and page 4
+"Caveats" notes KDA was not evaluated.  No formula is given.  The reading used
+here is KDA's own publication (Kimi Linear): Gated DeltaNet with the scalar gate
+replaced by a per-key-channel gate a_t in (0, 1]^N,
+    S_t = S_{t-1} Diag(a_t) (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
+in this [P][N] orientation (rows: value dim, columns: key dim), again evaluated
+as decay, error against the decayed state, rank-1 write.  The gate is per value
+head: alpha has shape [H, N].
 """
 from __future__ import annotations
 
@@ -63,10 +74,24 @@ def gdn_step(S, alpha, beta, v, k, q):
     return S_new, o
 
 
+def kda_step(S, alpha, beta, v, k, q):
+    """S <- S Diag(alpha_h) ; u = beta (v - S k) ; S <- S + u k^T ; o = S q.  alpha [H, N]."""
+    H = S.shape[0]
+    kh = expand_heads(k, H)
+    qh = expand_heads(q, H)
+    Sd = S * alpha[:, None, :]
+    u = beta[:, None] * (v - np.einsum("hpn,hn->hp", Sd, kh))
+    S_new = Sd + u[:, :, None] * kh[:, None, :]
+    o = np.einsum("hpn,hn->hp", S_new, qh)
+    return S_new, o
+
+
 def step(kind: str, S, rec):
     """Advance by one record ``rec`` = dict(alpha, beta, v, k, q) of float64 arrays."""
     if kind == "mamba2":
         return mamba2_step(S, rec["alpha"], rec["v"], rec["k"], rec["q"])
     if kind == "gdn":
         return gdn_step(S, rec["alpha"], rec["beta"], rec["v"], rec["k"], rec["q"])
+    if kind == "kda":
+        return kda_step(S, rec["alpha"], rec["beta"], rec["v"], rec["k"], rec["q"])
     raise ValueError(kind)

@@ -24,6 +24,10 @@ the stepwise recurrence (the definition).  A record is a dict with scalars
   for i from the newest record down: c = k_i . r; acc += decay(i -> t) b_i c v_i;
   r <- r - b_i c k_i; then o_t = acc + G_t S_0 r.  Mamba-2 is the case without
   the r update and with b_i = 1 in acc.
+* KDA (reading, derived the same way): with the per-channel gate a_i (a vector),
+  S_i r = S_{i-1} Diag(a_i)(r - b_i (k_i . r) k_i) + b_i (k_i . r) v_i, so the sweep
+  is c = b_i (k_i . r); acc += c v_i; r <- a_i o (r - c k_i), and o_t = acc + S_0 r.
+  The decays ride on r, so no scalar G or decay(i -> t) appears.
 """
 from __future__ import annotations
 
@@ -138,3 +142,14 @@ def query_transform_output(S0, recs: List[dict], q, kind: str) -> np.ndarray:
         else:
             acc = acc + Dm[i, t] * c * recs[i]["v"]
     return acc + gamma(a)[t] * (S0 @ r)
+
+
+def kda_query_transform_output(S0, recs: List[dict], q) -> np.ndarray:
+    """KDA output over the window ``recs`` (``alpha`` an [N] vector per record)."""
+    r = np.array(q, np.float64)
+    acc = np.zeros(S0.shape[0])
+    for rec in reversed(recs):
+        c = rec["beta"] * (rec["k"] @ r)
+        acc = acc + c * rec["v"]
+        r = np.asarray(rec["alpha"], np.float64) * (r - c * rec["k"])
+    return acc + S0 @ r

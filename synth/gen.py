@@ -13,6 +13,8 @@ Distributions (per the workload descriptions):
   k, q ~ N(0, 1/N) (the second parameter is the variance).
 * Gated DeltaNet: alpha = exp(-U(0, 0.5)); beta ~ U(0, 1); v ~ N(0, 1);
   k, q ~ N(0, 1) then scaled to unit L2 norm (in float64, before the cast).
+* KDA: as Gated DeltaNet, with alpha = exp(-U(0, 0.5)) drawn per (head, key
+  channel) instead of per head.
 * Initial state S0 ~ N(0, 0.1) (variance) in float32, or zero.
 * Accepted draft count per (sequence, verify step) ~ U{0, ..., T}.
 """
@@ -85,8 +87,8 @@ def _record(wl: Workload, g: np.random.Generator, hp: Dict[str, np.ndarray]):
         v = g.standard_normal((H, P))
         k = g.standard_normal((G, N)) / np.sqrt(N)
         q = g.standard_normal((G, N)) / np.sqrt(N)
-    elif wl.kind == "gdn":
-        alpha = np.exp(-g.uniform(0.0, 0.5, size=H))
+    elif wl.kind in ("gdn", "kda"):
+        alpha = np.exp(-g.uniform(0.0, 0.5, size=H if wl.kind == "gdn" else (H, N)))
         beta = g.uniform(0.0, 1.0, size=H)
         v = g.standard_normal((H, P))
         k = g.standard_normal((G, N))
@@ -102,8 +104,8 @@ def _empty(wl: Workload, lead: tuple) -> Dict[str, Optional[np.ndarray]]:
     dt = np.float32 if wl.in_dtype == "fp32" else np.uint16
     H, G, P, N = wl.n_heads, wl.n_qk_heads, wl.dv, wl.dk
     return {
-        "alpha": np.zeros(lead + (H,), dt),
-        "beta": np.zeros(lead + (H,), dt) if wl.kind == "gdn" else None,
+        "alpha": np.zeros(lead + ((H, N) if wl.kind == "kda" else (H,)), dt),
+        "beta": np.zeros(lead + (H,), dt) if wl.kind in ("gdn", "kda") else None,
         "v": np.zeros(lead + (H, P), dt),
         "k": np.zeros(lead + (G, N), dt),
         "q": np.zeros(lead + (G, N), dt),

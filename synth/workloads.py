@@ -1,4 +1,4 @@
-"""The five synthetic workloads of the ReplaySSM decode path.
+"""The synthetic workloads of the ReplaySSM decode path.
 
 Shapes follow the pages' problem statement: a Mamba-2 layer whose FP32 state is
 4 MiB per sequence (128 heads x 64 x 128 x 4 B; page "ReplaySSM caches SSM
@@ -6,7 +6,10 @@ inputs instead of state", section "What shipped"), a 16-record window (same
 section), batch 256 for standard decode and batch 512 with T = 4 drafts for
 speculative decoding (same page, evaluation paragraph), and a Gated DeltaNet
 layer with two value heads per key/query head (same section, chunkwise-verify
-paragraph).
+paragraph).  The KDA layer (page 4 "Why it matters": the reframing carries over to
+KDA's delta-rule update; not evaluated on the pages) takes the head shape of the
+published Kimi Linear model: 32 heads of 128 x 128, one key/query head per value
+head, with the Gated DeltaNet workload's batch, window and draft count.
 """
 from __future__ import annotations
 
@@ -17,7 +20,7 @@ from typing import Dict
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mamba2" or "gdn"
+    kind: str            # "mamba2", "gdn" or "kda"
     batch: int
     n_heads: int         # H, value heads
     n_qk_heads: int      # G, key/query heads (H % G == 0)
@@ -64,6 +67,11 @@ WORKLOADS: Dict[str, Workload] = {
                          dv=128, dk=128, in_dtype="bf16", L=16, t_max=4, capacity=19,
                          decode_steps=256, verify_steps=256, read_copy="none",
                          seed=_BASE_SEED + 3),
+    # Kimi Delta Attention: per-key-channel gates, 32 heads of 128 x 128, decode then verify
+    "kda_b256": Workload("kda_b256", "kda", batch=256, n_heads=32, n_qk_heads=32,
+                         dv=128, dk=128, in_dtype="bf16", L=16, t_max=4, capacity=19,
+                         decode_steps=256, verify_steps=256, read_copy="none",
+                         seed=_BASE_SEED + 5),
     # low-precision read copy of the fp32 checkpoint (fp8 e4m3; MXFP4 variant)
     "m2_readcopy_b256": Workload("m2_readcopy_b256", "mamba2", batch=256, n_heads=128,
                                  n_qk_heads=128, dv=64, dk=128, in_dtype="bf16", L=16,
