@@ -92,10 +92,11 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
   for (int i = 0; i < acc; ++i) {
     if (s_path[i] == i) continue;                            // already in place (uniform)
     const int src = ring_add(slot0, s_path[i], C), dst = ring_add(slot0, i, C);
-    // alpha (and beta) of every value head
+    // scalar alpha (Mamba-2, GDN) and beta (GDN, KDA) of every value head
+    const int f0 = g.kind == RSSM_KIND_KDA ? 1 : 0, f1 = g.kind == RSSM_KIND_MAMBA2 ? 1 : 2;
     for (int h = t; h < H; h += kThreads) {
       const size_t hr = (size_t)b * H + h;
-      for (int f = 0; f < (g.kind == RSSM_KIND_GDN ? 2 : 1); ++f) {
+      for (int f = f0; f < f1; ++f) {
         const int64_t base = f == 0 ? g.off_alpha : g.off_beta;
         if (es == 2)
           *(uint16_t *)(a.ring + base + (hr * C + dst) * 2) = *(const uint16_t *)(a.ring + base + (hr * C + src) * 2);
@@ -113,6 +114,17 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       const uint8_t *ps = a.ring + base + (kr * C + src) * N * es + part * 16;
       uint8_t *pd = a.ring + base + (kr * C + dst) * N * es + part * 16;
       *(uint4 *)pd = *(const uint4 *)ps;
+    }
+    // KDA: the alpha row (dk elements, a whole number of 16-byte chunks) of every value head
+    if (g.kind == RSSM_KIND_KDA) {
+      const int cpa = N * es / 16, na = H * cpa;
+      for (int c = t; c < na; c += kThreads) {
+        const int h = c / cpa, part = c - h * cpa;
+        const size_t hr = (size_t)b * H + h;
+        const uint8_t *ps = a.ring + g.off_alpha + (hr * C + src) * N * es + part * 16;
+        uint8_t *pd = a.ring + g.off_alpha + (hr * C + dst) * N * es + part * 16;
+        *(uint4 *)pd = *(const uint4 *)ps;
+      }
     }
     // v of every value head
     if (vec) {
@@ -195,6 +207,11 @@ hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStrea
 #define RSSM_ROUTE(FN)                                                   \
   {                                                                      \
     const int stg = stage_of(a);                                         \
+    if (a.g.kind == RSSM_KIND_KDA) {                                     \
+      if (stg == kStageBf16) return KindLaunch<RSSM_KIND_KDA, kStageBf16>::FN(a, s); \
+      if (stg == kStageF32) return KindLaunch<RSSM_KIND_KDA, kStageF32>::FN(a, s);   \
+      return KindLaunch<RSSM_KIND_KDA, kStageScalar>::FN(a, s);          \
+    }                                                                    \
     if (a.g.kind == RSSM_KIND_GDN) {                                     \
       if (stg == kStageBf16) return KindLaunch<RSSM_KIND_GDN, kStageBf16>::FN(a, s); \
       if (stg == kStageF32) return KindLaunch<RSSM_KIND_GDN, kStageF32>::FN(a, s);   \

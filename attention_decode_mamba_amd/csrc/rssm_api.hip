@@ -15,7 +15,7 @@ bool dk_ok(int dk) { return dk == 32 || dk == 64 || dk == 128 || dk == 256; }
 
 int check_cfg(const rssm_config *c) {
   if (!c) return RSSM_E_NULL;
-  if (c->kind != RSSM_KIND_MAMBA2 && c->kind != RSSM_KIND_GDN) return RSSM_E_DTYPE;
+  if (c->kind != RSSM_KIND_MAMBA2 && c->kind != RSSM_KIND_GDN && c->kind != RSSM_KIND_KDA) return RSSM_E_DTYPE;
   if (c->in_dtype != RSSM_DTYPE_F32 && c->in_dtype != RSSM_DTYPE_BF16) return RSSM_E_DTYPE;
   if (c->read_copy < RSSM_READ_NONE || c->read_copy > RSSM_READ_MXFP4) return RSSM_E_DTYPE;
   if (c->batch < 0 || c->n_heads < 1 || c->n_qk_heads < 1) return RSSM_E_SHAPE;
@@ -30,6 +30,7 @@ int check_cfg(const rssm_config *c) {
   const int64_t rows_v = (int64_t)c->batch * c->n_heads, rows_k = (int64_t)c->batch * c->n_qk_heads;
   const int64_t slots = std::max<int64_t>(c->capacity, c->t_max);
   if (rows_v * slots * c->dv >= lim || rows_k * slots * c->dk >= lim) return RSSM_E_SHAPE;
+  if (c->kind == RSSM_KIND_KDA && rows_v * slots * c->dk >= lim) return RSSM_E_SHAPE;
   if (lds_bytes(c->kind, c->capacity + 1, 1, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
   if (lds_bytes(c->kind, c->capacity, c->t_max, c->dv, c->dk) > (size_t)kMaxLdsBytes) return RSSM_E_SHAPE;
   return RSSM_OK;
@@ -40,10 +41,10 @@ void ring_layout(const rssm_config *c, int64_t off[5], int64_t *total) {
   const int64_t B = c->batch, H = c->n_heads, G = c->n_qk_heads, C = c->capacity;
   const int64_t P = c->dv, N = c->dk;
   int64_t o = 0;
-  off[0] = o;                                   // alpha [B][H][C]
-  o = align256(o + B * H * C * es);
-  off[1] = o;                                   // beta [B][H][C] (GDN only)
-  if (c->kind == RSSM_KIND_GDN) o = align256(o + B * H * C * es);
+  off[0] = o;                                   // alpha [B][H][C] (KDA: [B][H][C][N])
+  o = align256(o + B * H * C * (c->kind == RSSM_KIND_KDA ? N : 1) * es);
+  off[1] = o;                                   // beta [B][H][C] (GDN and KDA)
+  if (c->kind != RSSM_KIND_MAMBA2) o = align256(o + B * H * C * es);
   off[2] = o;                                   // v [B][H][C][P]
   o = align256(o + B * H * C * P * es);
   off[3] = o;                                   // k [B][G][C][N]
@@ -100,7 +101,7 @@ int check_state(const rssm_config *c, const rssm_state *st, bool need_ring) {
 int check_inputs(const rssm_config *c, const void *alpha, const void *beta, const void *v, const void *k,
                  const void *q, const float *out) {
   if (!alpha || !v || !k || !q || !out) return RSSM_E_NULL;
-  if (c->kind == RSSM_KIND_GDN && !beta) return RSSM_E_NULL;
+  if (c->kind != RSSM_KIND_MAMBA2 && !beta) return RSSM_E_NULL;
   const uintptr_t es = c->in_dtype == RSSM_DTYPE_BF16 ? 2 : 4;
   if (!aligned(alpha, es) || !aligned(v, es) || !aligned(k, es) || !aligned(q, es) || !aligned(out, 4))
     return RSSM_E_ALIGN;
@@ -128,10 +129,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_E_HIP; }
 
 // Rows can be moved in 16-byte chunks when a row is a whole number of chunks and every
 // input row starts on a 16-byte boundary (ring rows then do too: the ring is 256-aligned).
-int vec16_ok(const rssm_config *c, const void *v, const void *k, const void *q) {
+// KDA's alpha rows (dk elements) are staged like key rows.
+int vec16_ok(const rssm_config *c, const void *alpha, const void *v, const void *k, const void *q) {
   const int epc = c->in_dtype == RSSM_DTYPE_BF16 ? 8 : 4;
   if (c->dv % epc || c->dk % epc) return 0;
   if ((v && !aligned(v, 16)) || (k && !aligned(k, 16)) || (q && !aligned(q, 16))) return 0;
+  if (c->kind == RSSM_KIND_KDA && alpha && !aligned(alpha, 16)) return 0;
   return 1;
 }
 
@@ -199,7 +202,7 @@ int rssm_decode_step(const rssm_config *cfg, const rssm_state *st, const void *a
   a.k = k;
   a.q = q;
   a.out = y;
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_decode(a, stream));
 }
 
@@ -211,7 +214,7 @@ int rssm_flush(const rssm_config *cfg, const rssm_state *st, int32_t min_records
   if (cfg->batch == 0) return RSSM_OK;
   Args a = make_args(cfg, st);
   a.min_records = min_records;
-  a.vec16 = vec16_ok(cfg, nullptr, nullptr, nullptr);
+  a.vec16 = vec16_ok(cfg, nullptr, nullptr, nullptr, nullptr);
   return hip_status(launch_flush(a, stream));
 }
 
@@ -231,7 +234,7 @@ int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const v
   a.q = q;
   a.out = o;
   a.T = T;
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_verify(a, stream));
 }
 
@@ -270,7 +273,7 @@ int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T, co
   a.out = o;
   a.T = T;
   a.parent = parent;
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_verify(a, stream));
 }
 
@@ -295,7 +298,7 @@ int rssm_verify_fold(const rssm_config *cfg, const rssm_state *st, int32_t min_r
   a.T = T;
   a.parent = parent;
   a.min_records = min_records > 1 ? min_records : 1;  // the fold threshold of rssm_flush
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_verify(a, stream));
 }
 
@@ -338,7 +341,7 @@ int rssm_verify_snapshot(const rssm_config *cfg, float *snap, const int32_t *cur
   a.q = q;
   a.out = o;
   a.T = T;
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_verify_snapshot(a, stream));
 }
 
@@ -375,7 +378,7 @@ int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *
   a.k = k;
   a.q = q;
   a.out = y;
-  a.vec16 = vec16_ok(cfg, v, k, q);
+  a.vec16 = vec16_ok(cfg, alpha, v, k, q);
   return hip_status(launch_conventional(a, stream));
 }
 

@@ -397,6 +397,7 @@ __device__ __forceinline__ void readcopy_dot(const RCopy<N, RGW> &R, int fmt, co
 struct StageSpec {
   int nrec, n_ring, slot0, C, P, N, nq, bf16;
   int cpv_lg;                            // log2 of 16-byte chunks per value row, or -1
+  int avec;                              // alpha is an N-vector per record (KDA)
   const uint8_t *rA, *rB, *rV, *rK;      // ring regions
   int hrow, krow;                        // ring row (slot 0) of this value head / key head
   const void *iA, *iB, *iV, *iK, *iQ;    // inputs
@@ -431,25 +432,30 @@ struct StageRegs {
 };
 
 __device__ __forceinline__ int stage_chunks(const StageSpec &sp, int epc) {
-  return sp.nrec * (sp.P / epc) + sp.nrec * (sp.N / epc) + sp.nq * (sp.N / epc);
+  return sp.nrec * (sp.P / epc) + sp.nrec * (sp.N / epc) * (1 + sp.avec) + sp.nq * (sp.N / epc);
 }
 
 // Issue one round of staging loads.  Every lane issues every load (idle chunks re-read the
 // last valid chunk and are marked dst = -1), so the loads form straight-line code.
-template <int U, bool BF, bool HASB>
+// Chunk order: v rows, k rows, alpha rows (AVEC: KDA's per-channel gates), query rows.
+template <int U, bool BF, bool HASB, bool AVEC>
 __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R, int base, float *lds, int t,
                                             bool with_scalars) {
   constexpr int es = BF ? 2 : 4;
   constexpr int epc = 16 / es;
   const int cpv = sp.P / epc, cpk = sp.N / epc;
-  const int nV = sp.nrec * cpv, nK = sp.nrec * cpk, total = nV + nK + sp.nq * cpk;
+  const int nV = sp.nrec * cpv, nK = sp.nrec * cpk, nA = AVEC ? nK : 0, total = nV + nK + nA + sp.nq * cpk;
   if (with_scalars) {
     const int j = t < sp.nrec ? t : sp.nrec - 1;
     const bool ring = j < sp.n_ring;
     const int ri = sp.hrow + ring_slot(sp, j);
     const int ii = sp.ia0 + (j - sp.n_ring) * sp.ias;
-    const uint8_t *pa = ring ? sp.rA + (size_t)ri * es : (const uint8_t *)sp.iA + (size_t)ii * es;
-    R.a = BF ? bf16f(*(const uint16_t *)pa) : *(const float *)pa;
+    if (!AVEC) {
+      const uint8_t *pa = ring ? sp.rA + (size_t)ri * es : (const uint8_t *)sp.iA + (size_t)ii * es;
+      R.a = BF ? bf16f(*(const uint16_t *)pa) : *(const float *)pa;
+    } else {
+      R.a = 0.f;
+    }
     if (HASB) {
       const uint8_t *pb = ring ? sp.rB + (size_t)ri * es : (const uint8_t *)sp.iB + (size_t)ii * es;
       R.b = BF ? bf16f(*(const uint16_t *)pb) : *(const float *)pb;
@@ -481,8 +487,14 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
         bp = ring ? sp.rK : (const uint8_t *)sp.iK;
         idx = ring ? (sp.krow + ring_slot(sp, j)) * sp.N + e : sp.ik0 + (j - sp.n_ring) * sp.iks + e;
         dst = (int)(sp.K - lds) + j * (sp.N + 4) + e;
+      } else if (AVEC && c < nV + nK + nA) {
+        const int l = c - nV - nK, j = l / cpk, e = (l - j * cpk) * epc;
+        const bool ring = j < sp.n_ring;
+        bp = ring ? sp.rA : (const uint8_t *)sp.iA;
+        idx = ring ? (sp.hrow + ring_slot(sp, j)) * sp.N + e : (sp.ia0 + (j - sp.n_ring) * sp.ias) * sp.N + e;
+        dst = (int)(sp.A - lds) + j * (sp.N + 4) + e;
       } else {
-        const int l = c - nV - nK, r = l / cpk, e = (l - r * cpk) * epc;
+        const int l = c - nV - nK - nA, r = l / cpk, e = (l - r * cpk) * epc;
         bp = (const uint8_t *)sp.iQ;
         idx = sp.iq0 + r * sp.iqs + e;
         dst = (int)(sp.Q - lds) + r * sp.N + e;
@@ -493,11 +505,11 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
   }
 }
 
-template <int U, bool BF>
+template <int U, bool BF, bool AVEC>
 __device__ __forceinline__ void stage_commit(const StageSpec &sp, const StageRegs<U> &R, float *lds, int t,
                                              bool with_scalars) {
   if (with_scalars && t < sp.nrec) {
-    sp.A[t] = R.a;
+    if (!AVEC) sp.A[t] = R.a;
     sp.Bt[t] = R.b;
   }
 #pragma unroll
@@ -520,19 +532,26 @@ __device__ __forceinline__ void stage_commit(const StageSpec &sp, const StageReg
 // Element-wise staging for shapes that cannot use 16-byte chunks (e.g. P % 8 != 0 with bf16).
 __device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
   for (int j = t; j < sp.nrec; j += kThreads) {
-    float al, be = 0.f;
+    float al = 0.f, be = 0.f;
     if (j < sp.n_ring) {
       const int i = sp.hrow + ring_slot(sp, j);
-      al = ld_in(sp.rA, i, sp.bf16);
+      if (!sp.avec) al = ld_in(sp.rA, i, sp.bf16);
       if (sp.rB) be = ld_in(sp.rB, i, sp.bf16);
     } else {
       const int i = sp.ia0 + (j - sp.n_ring) * sp.ias;
-      al = ld_in(sp.iA, i, sp.bf16);
+      if (!sp.avec) al = ld_in(sp.iA, i, sp.bf16);
       if (sp.iB) be = ld_in(sp.iB, i, sp.bf16);
     }
-    sp.A[j] = al;
+    if (!sp.avec) sp.A[j] = al;
     sp.Bt[j] = be;
   }
+  if (sp.avec)
+    for (int e = t; e < sp.nrec * sp.N; e += kThreads) {
+      const int j = e / sp.N, n = e - j * sp.N;
+      sp.A[j * (sp.N + 4) + n] = j < sp.n_ring
+                                     ? ld_in(sp.rA, (sp.hrow + ring_slot(sp, j)) * sp.N + n, sp.bf16)
+                                     : ld_in(sp.iA, (sp.ia0 + (j - sp.n_ring) * sp.ias) * sp.N + n, sp.bf16);
+    }
   for (int e = t; e < sp.nrec * sp.P; e += kThreads) {
     const int j = e / sp.P, p = e - j * sp.P;
     sp.V[e] = j < sp.n_ring ? ld_in(sp.rV, (sp.hrow + ring_slot(sp, j)) * sp.P + p, sp.bf16)
@@ -564,14 +583,15 @@ __device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L
   sp.nq = nq;
   sp.bf16 = g.bf16;
   sp.cpv_lg = g.cpv_lg;
+  sp.avec = KIND == RSSM_KIND_KDA;
   sp.rA = a.ring + g.off_alpha;
-  sp.rB = KIND == RSSM_KIND_GDN ? a.ring + g.off_beta : nullptr;
+  sp.rB = KIND != RSSM_KIND_MAMBA2 ? a.ring + g.off_beta : nullptr;
   sp.rV = a.ring + g.off_v;
   sp.rK = a.ring + g.off_k;
   sp.hrow = (b * g.H + hh) * g.C;
   sp.krow = (b * g.G + gq) * g.C;
   sp.iA = a.alpha;
-  sp.iB = KIND == RSSM_KIND_GDN ? a.beta : nullptr;
+  sp.iB = KIND != RSSM_KIND_MAMBA2 ? a.beta : nullptr;
   sp.iV = a.v;
   sp.iK = a.k;
   sp.iQ = a.q;
@@ -586,34 +606,36 @@ __device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L
 
 // Stage a tile's records with the checkpoint loads in flight: record loads are issued
 // first, then `issue_tile()` (the checkpoint or read-copy loads), then the LDS writes.
-template <int U, bool BF, bool HASB, class IssueTile>
+template <int U, bool BF, bool HASB, bool AVEC, class IssueTile>
 __device__ __forceinline__ void stage_vec_with_tile(const StageSpec &sp, float *lds, int t, IssueTile &&issue_tile) {
   StageRegs<U> SR;
-  stage_issue<U, BF, HASB>(sp, SR, 0, lds, t, true);
+  stage_issue<U, BF, HASB, AVEC>(sp, SR, 0, lds, t, true);
   issue_tile();
-  stage_commit<U, BF>(sp, SR, lds, t, true);
+  stage_commit<U, BF, AVEC>(sp, SR, lds, t, true);
   const int total = stage_chunks(sp, BF ? 8 : 4);
   for (int base = kThreads * U; base < total; base += kThreads * U) {
-    stage_issue<U, BF, HASB>(sp, SR, base, lds, t, false);
-    stage_commit<U, BF>(sp, SR, lds, t, false);
+    stage_issue<U, BF, HASB, AVEC>(sp, SR, base, lds, t, false);
+    stage_commit<U, BF, AVEC>(sp, SR, lds, t, false);
   }
 }
 
 // STG (kStage*) is chosen by the launcher, so a kernel carries one staging path: with
 // several, the tile registers loaded on each path meet in one merge and the fold loop that
 // follows worked on a copy of them (twice the tile's registers live at once).
-template <int U, bool HASB, int STG, class IssueTile>
+template <int U, int KIND, int STG, class IssueTile>
 __device__ __forceinline__ void stage_with_tile(const StageSpec &sp, float *lds, int t, IssueTile &&issue_tile) {
   if constexpr (STG == kStageScalar) {
     issue_tile();
     stage_scalar(sp, t);
   } else {
-    stage_vec_with_tile<U, STG == kStageBf16, HASB>(sp, lds, t, issue_tile);
+    stage_vec_with_tile<U, STG == kStageBf16, KIND != RSSM_KIND_MAMBA2, KIND == RSSM_KIND_KDA>(sp, lds, t,
+                                                                                           issue_tile);
   }
 }
 
 // Append record row j of LDS (and query row qr) to ring slot `slot` (values are exact
-// widenings of the inputs, so narrowing back to bf16 reproduces the input bits).
+// widenings of the inputs, so narrowing back to bf16 reproduces the input bits).  KDA's
+// alpha is an N-vector per value head, stored like a key row.
 template <int KIND, int N>
 __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *lds, int b, int hh, int gq, int j,
                                 int qr, int slot, int t) {
@@ -628,26 +650,30 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
     uint16_t *rK = (uint16_t *)(a.ring + g.off_k);
     uint16_t *rQ = (uint16_t *)(a.ring + g.off_q);
     if (t == 0) {
-      rA[hr] = (uint16_t)(__float_as_uint(lds[L.alpha + j]) >> 16);
-      if (KIND == RSSM_KIND_GDN)
+      if (KIND != RSSM_KIND_KDA) rA[hr] = (uint16_t)(__float_as_uint(lds[L.alpha + j]) >> 16);
+      if (KIND != RSSM_KIND_MAMBA2)
         ((uint16_t *)(a.ring + g.off_beta))[hr] = (uint16_t)(__float_as_uint(lds[L.beta + j]) >> 16);
     }
     if (a.vec16) {
-      // 8 elements per 16-byte store: v (P/8 chunks), then k and q (N/8 each, key-head leader only)
-      const int cv = P / 8, ck = N / 8;
-      const int total = cv + (lead ? 2 * ck : 0);
+      // 8 elements per 16-byte store: v (P/8 chunks), KDA alpha (N/8), then k and q (N/8
+      // each, key-head leader only)
+      const int cv = P / 8, ck = N / 8, ca = KIND == RSSM_KIND_KDA ? ck : 0;
+      const int total = cv + ca + (lead ? 2 * ck : 0);
       for (int c = t; c < total; c += kThreads) {
         const float *src;
         uint16_t *dst;
         if (c < cv) {
           src = lds + L.V + j * P + 8 * c;
           dst = rV + hr * P + 8 * c;
-        } else if (c < cv + ck) {
-          src = lds + L.K + j * (N + 4) + 8 * (c - cv);
-          dst = rK + kr + 8 * (c - cv);
+        } else if (c < cv + ca) {
+          src = lds + L.alpha + j * (N + 4) + 8 * (c - cv);
+          dst = rA + hr * N + 8 * (c - cv);
+        } else if (c < cv + ca + ck) {
+          src = lds + L.K + j * (N + 4) + 8 * (c - cv - ca);
+          dst = rK + kr + 8 * (c - cv - ca);
         } else {
-          src = lds + L.q + qr * N + 8 * (c - cv - ck);
-          dst = rQ + kr + 8 * (c - cv - ck);
+          src = lds + L.q + qr * N + 8 * (c - cv - ca - ck);
+          dst = rQ + kr + 8 * (c - cv - ca - ck);
         }
         const float4 x0 = *(const float4 *)src, x1 = *(const float4 *)(src + 4);
         uint4 w;
@@ -659,6 +685,9 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
       }
     } else {
       for (int p = t; p < P; p += kThreads) rV[hr * P + p] = (uint16_t)(__float_as_uint(lds[L.V + j * P + p]) >> 16);
+      if (KIND == RSSM_KIND_KDA)
+        for (int n = t; n < N; n += kThreads)
+          rA[hr * N + n] = (uint16_t)(__float_as_uint(lds[L.alpha + j * (N + 4) + n]) >> 16);
       if (lead)
         for (int n = t; n < N; n += kThreads) {
           rK[kr + n] = (uint16_t)(__float_as_uint(lds[L.K + j * (N + 4) + n]) >> 16);
@@ -671,10 +700,12 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
     float *rK = (float *)(a.ring + g.off_k);
     float *rQ = (float *)(a.ring + g.off_q);
     if (t == 0) {
-      rA[hr] = lds[L.alpha + j];
-      if (KIND == RSSM_KIND_GDN) ((float *)(a.ring + g.off_beta))[hr] = lds[L.beta + j];
+      if (KIND != RSSM_KIND_KDA) rA[hr] = lds[L.alpha + j];
+      if (KIND != RSSM_KIND_MAMBA2) ((float *)(a.ring + g.off_beta))[hr] = lds[L.beta + j];
     }
     for (int p = t; p < P; p += kThreads) rV[hr * P + p] = lds[L.V + j * P + p];
+    if (KIND == RSSM_KIND_KDA)
+      for (int n = t; n < N; n += kThreads) rA[hr * N + n] = lds[L.alpha + j * (N + 4) + n];
     if (lead)
       for (int n = t; n < N; n += kThreads) {
         rK[kr + n] = lds[L.K + j * (N + 4) + n];
@@ -817,6 +848,59 @@ __device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int
   }
 }
 
+// Sum over the 64 lanes of a wave (all lanes active); every lane gets the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// KDA query transform for one query over records 0..n-1 (one wave, all lanes active).
+// With the per-channel gate a_i, S_i r = S_{i-1} Diag(a_i) (r - b_i (k_i . r) k_i)
+// + b_i (k_i . r) v_i, so from the newest record down: c_i = b_i (k_i . r),
+// r <- a_i o (r - c_i k_i).  Writes c_i to the coef row (0 for records off the query's
+// path, which act as neutral records), the final r to the r row, and G = 1 (the decays
+// are carried by r).  Lane l holds elements l + 64 e.
+template <int N>
+__device__ void kda_sweep_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
+                               int hb = 1 << 30, uint32_t anc = 0) {
+  constexpr int E = (N + 63) / 64;
+  const float *beta = lds + L.beta;
+  float *coef = lds + L.coef + tau * cap;
+  float r[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = lane + 64 * e;
+    r[e] = idx < N ? lds[L.q + tau * N + idx] : 0.f;
+  }
+  for (int i = n - 1; i >= 0; --i) {
+    if (!on_path(i, hb, anc)) {                      // uniform across the wave
+      if (lane == 0) coef[i] = 0.f;
+      continue;
+    }
+    const float *k = lds + L.K + i * (N + 4);
+    const float *al = lds + L.alpha + i * (N + 4);
+    float p = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = lane + 64 * e;
+      if (idx < N) p = fmaf(k[idx], r[e], p);
+    }
+    const float c = beta[i] * wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = lane + 64 * e;
+      if (idx < N) r[e] = al[idx] * fmaf(-c, k[idx], r[e]);
+    }
+    if (lane == 0) coef[i] = c;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = lane + 64 * e;
+    if (idx < N) lds[L.r + tau * N + idx] = r[e];
+  }
+  if (lane == 0) lds[L.gam + tau] = 1.f;
+}
+
 // ---------------------------------------------------------------- folds
 // Mamba-2 fold: S <- G S + sum_j d_j v_j k_j^T (decays in L.dec, G in L.gam).
 template <int N, int RGW>
@@ -896,6 +980,58 @@ __device__ __forceinline__ void fold_gdn(Frag<N, RGW> &F, const float *lds, cons
   }
 }
 
+// KDA fold, one per-channel gated delta-rule update per record in registers:
+// S <- S Diag(a) ; u = b (v - S k) ; S <- S + u k^T (a: the record's alpha row in LDS).
+template <int N, int RGW>
+__device__ __forceinline__ void fold_kda(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P,
+                                         int wave, int lane) {
+  const int c = frag_col(lane);
+  for (int j = 0; j < nrec; ++j) {
+    const float be = lds[L.beta + j];
+    const float *kr = lds + L.K + j * (N + 4) + c;
+    const float *ar = lds + L.alpha + j * (N + 4) + c;
+    float w[RGW];
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) w[i] = 0.f;
+#pragma unroll
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f), af = *(const float4 *)(ar + 32 * f);
+      const float4 akf = make_float4(af.x * kf.x, af.y * kf.y, af.z * kf.z, af.w * kf.w);
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], akf, w[i]);
+    }
+    float u[RGW];
+#pragma unroll
+    for (int i = 0; i < RGW; ++i) {
+      const float wi = oct_sum(w[i]);
+      const int row = frag_row(wave, lane, i);
+      const float vr = (row < P) ? lds[L.V + j * P + row] : 0.f;
+      u[i] = be * (vr - wi);
+    }
+#pragma unroll
+    for (int f = 0; f < N / 32; ++f) {
+      const float4 kf = *(const float4 *)(kr + 32 * f), af = *(const float4 *)(ar + 32 * f);
+#pragma unroll
+      for (int i = 0; i < RGW; ++i) {
+        F.s[i][f].x = fmaf(af.x, F.s[i][f].x, u[i] * kf.x);
+        F.s[i][f].y = fmaf(af.y, F.s[i][f].y, u[i] * kf.y);
+        F.s[i][f].z = fmaf(af.z, F.s[i][f].z, u[i] * kf.z);
+        F.s[i][f].w = fmaf(af.w, F.s[i][f].w, u[i] * kf.w);
+      }
+    }
+  }
+}
+
+// Delta-rule fold of either gated kind.
+template <int KIND, int N, int RGW>
+__device__ __forceinline__ void fold_delta(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P,
+                                           int wave, int lane) {
+  if constexpr (KIND == RSSM_KIND_KDA)
+    fold_kda(F, lds, L, nrec, P, wave, lane);
+  else
+    fold_gdn(F, lds, L, nrec, P, wave, lane);
+}
+
 // Output rows: y[row] = G * (S x)[row] + sum_{j < n} w_j v_j[row], where w_j = dec[j] * coef[j]
 // (Mamba-2: decay times k_j . q) or w_j = coef[j] (GDN: already d_j b_j c_j; dec == null).
 // The 8 lanes of a row take records j = l%8 mod 8.
@@ -925,7 +1061,7 @@ __device__ __forceinline__ void write_rows(const float (&part)[RGW], float G, co
 // serves non-fold steps from it.
 template <int KIND, int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
-  constexpr int U = (KIND == RSSM_KIND_GDN || RGW > 2) ? 4 : 2;
+  constexpr int U = (KIND != RSSM_KIND_MAMBA2 || RGW > 2) ? 4 : 2;
   constexpr bool RC = RCF != RSSM_READ_NONE;
   extern __shared__ float lds[];
   const Geom &g = a.g;
@@ -958,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   float *yout = a.out + (b * g.H + hh) * P;
   if (flush) {
     Frag<N, RGW> F;
-    stage_with_tile<U, KIND == RSSM_KIND_GDN, STG>(sp, lds, t,
+    stage_with_tile<U, KIND, STG>(sp, lds, t,
                                                [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
     __syncthreads();
     if (KIND == RSSM_KIND_MAMBA2) {
@@ -966,7 +1102,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       __syncthreads();
       fold_m2(F, lds, L, nrec, P, wave, lane);
     } else {
-      fold_gdn(F, lds, L, nrec, P, wave, lane);
+      fold_delta<KIND>(F, lds, L, nrec, P, wave, lane);
     }
     frag_store(F, tileS, P, wave, lane);
     frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
@@ -976,7 +1112,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
   } else {
     Frag<N, RGW> F;
     RCopy<N, RGW> RCR;
-    stage_with_tile<U, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() {
+    stage_with_tile<U, KIND, STG>(sp, lds, t, [&]() {
       if (RC)
         readcopy_load(RCR, RCF, a.s_read, a.s_read_scale, tile, P, wave, lane);
       else
@@ -991,6 +1127,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       __syncthreads();
       x = lds + L.q;
       dec = lds + L.dec;
+    } else if (KIND == RSSM_KIND_KDA) {
+      if (wave == 0) kda_sweep_wave<N>(lds, L, cap, nrec, 0, lane);
+      __syncthreads();
+      x = lds + L.r;
     } else {
       gram_and_kq<N>(lds, L, cap, nrec, 1, t);
       __syncthreads();
@@ -1059,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   // tree, the previous draft).  Loaded with the records, resolved to ancestor masks after.
   const int my_parent = t < T ? (a.parent ? a.parent[b * T + t] : t - 1) : 0;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND, STG>(sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
   int *const par = (int *)(lds + L.anc) + T;
   uint32_t *const anc = (uint32_t *)(lds + L.anc);
   if (t < T) par[t] = my_parent;
@@ -1085,7 +1225,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
       __syncthreads();
       fold_m2(F, lds, L, hb, P, wave, lane);
     } else {
-      fold_gdn(F, lds, L, hb, P, wave, lane);
+      fold_delta<KIND>(F, lds, L, hb, P, wave, lane);
     }
     frag_store(F, tileS, P, wave, lane);
     frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
@@ -1102,7 +1242,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   const int r0 = fold ? hb : 0;
   const int hv = hb - r0;              // committed records every query sees
   LdsLayout Lv = L;
-  Lv.alpha += r0;
+  Lv.alpha += KIND == RSSM_KIND_KDA ? r0 * (N + 4) : r0;
   Lv.beta += r0;
   Lv.K += r0 * (N + 4);
   Lv.V += r0 * P;
@@ -1118,6 +1258,11 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     __syncthreads();
     xbase = lds + Lv.q;
     dec = lds + Lv.dec;
+  } else if (KIND == RSSM_KIND_KDA) {
+    for (int tau = wave; tau < T; tau += kWaves)
+      kda_sweep_wave<N>(lds, Lv, cap, hv + tau + 1, tau, lane, hv, anc[tau]);
+    __syncthreads();
+    xbase = lds + Lv.r;
   } else {
     gram_and_kq<N>(lds, Lv, cap, hv + T, T, t);
     __syncthreads();
@@ -1167,14 +1312,14 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, nrec, 0, 0);
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
   if (KIND == RSSM_KIND_MAMBA2) {
     if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
     __syncthreads();
     fold_m2(F, lds, L, nrec, P, wave, lane);
   } else {
-    fold_gdn(F, lds, L, nrec, P, wave, lane);
+    fold_delta<KIND>(F, lds, L, nrec, P, wave, lane);
   }
   frag_store(F, tileS, P, wave, lane);
   frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
@@ -1182,10 +1327,20 @@ __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
 }
 
 // One recurrence step on the register tile with staged record j:
-// Mamba-2 S <- a S + v k^T; Gated DeltaNet S <- a S + u k^T with u = b (v - a S k).
+// Mamba-2 S <- a S + v k^T; Gated DeltaNet S <- a S + u k^T with u = b (v - a S k);
+// KDA: the fold's per-channel update.
 template <int KIND, int N, int RGW>
 __device__ __forceinline__ void step_record(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int j, int P,
                                             int wave, int lane) {
+  if constexpr (KIND == RSSM_KIND_KDA) {
+    LdsLayout Lj = L;
+    Lj.alpha += j * (N + 4);
+    Lj.beta += j;
+    Lj.K += j * (N + 4);
+    Lj.V += j * P;
+    fold_kda(F, lds, Lj, 1, P, wave, lane);
+    return;
+  }
   const int c = frag_col(lane);
   const float al = lds[L.alpha + j];
   const float *kr = lds + L.K + j * (N + 4) + c;
@@ -1243,7 +1398,7 @@ __global__ __launch_bounds__(kThreads) void k_conventional(Args a) {
   sp.ik0 = (b * g.G + gq) * N;
   sp.iq0 = sp.ik0;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
+  stage_with_tile<4, KIND, STG>(sp, lds, t, [&]() { frag_load<N, RGW, false>(F, tileS, P, wave, lane); });
   __syncthreads();
   step_record<KIND, N, RGW>(F, lds, L, 0, P, wave, lane);
   frag_store(F, tileS, P, wave, lane);
@@ -1284,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void k_verify_snapshot(Args a) {
   sp.iq0 = sp.ik0;
   sp.iqs = sp.iks;
   Frag<N, RGW> F;
-  stage_with_tile<4, KIND == RSSM_KIND_GDN, STG>(sp, lds, t, [&]() {
+  stage_with_tile<4, KIND, STG>(sp, lds, t, [&]() {
     frag_load<N, RGW, true>(F, base + (int64_t)cur * g.H * PN, P, wave, lane);
   });
   __syncthreads();

@@ -55,6 +55,7 @@ struct Args {
 };
 
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
+// Rows of N floats (K, KDA's alpha) are padded by 4 floats.
 struct LdsLayout {
   int alpha, beta, dec, coef, cc, gam, misc, anc, q, r, K, V, gram, total;
 };
@@ -64,7 +65,7 @@ __host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
 __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P, int N) {
   LdsLayout l;
   int o = 0;
-  l.alpha = o; o += up4(cap);
+  l.alpha = o; o += (kind == RSSM_KIND_KDA) ? cap * (N + 4) : up4(cap);   // KDA: an N-vector per record
   l.beta = o;  o += up4(cap);
   l.dec = o;   o += up4(T * cap);
   l.coef = o;  o += up4(T * cap);

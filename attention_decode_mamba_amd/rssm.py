@@ -33,6 +33,7 @@ RSSM_DEVERR_TREE = 8
 
 RSSM_KIND_MAMBA2 = 0
 RSSM_KIND_GDN = 1
+RSSM_KIND_KDA = 2
 RSSM_DTYPE_F32 = 0
 RSSM_DTYPE_BF16 = 1
 RSSM_READ_NONE = 0

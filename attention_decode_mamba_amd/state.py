@@ -7,7 +7,7 @@ import torch
 
 from . import rssm as R
 
-_KIND = {"mamba2": R.RSSM_KIND_MAMBA2, "gdn": R.RSSM_KIND_GDN}
+_KIND = {"mamba2": R.RSSM_KIND_MAMBA2, "gdn": R.RSSM_KIND_GDN, "kda": R.RSSM_KIND_KDA}
 _DTYPE = {"fp32": R.RSSM_DTYPE_F32, "bf16": R.RSSM_DTYPE_BF16}
 _READ = {"none": R.RSSM_READ_NONE, "fp8": R.RSSM_READ_FP8, "mxfp4": R.RSSM_READ_MXFP4}
 
@@ -61,7 +61,8 @@ class DeviceState:
         return (self.n_committed[: B * H].view(B, H), self.n_ckpt[: B * H].view(B, H))
 
     def ring_arrays(self):
-        """Typed views of the ring regions: alpha, beta (GDN) [B,H,C], v [B,H,C,P], k, q [B,G,C,N]."""
+        """Typed views of the ring regions: alpha [B,H,C] (KDA [B,H,C,N]), beta (GDN, KDA) [B,H,C],
+        v [B,H,C,P], k, q [B,G,C,N]."""
         c = self.cfg
         off = R.rssm_ring_offsets(c)
         es = 2 if c.in_dtype == R.RSSM_DTYPE_BF16 else 4
@@ -70,11 +71,12 @@ class DeviceState:
 
         def view(o, n, shape):
             return self.ring[o: o + n * es].view(dt).view(*shape)
-        out = {"alpha": view(off[0], B * H * C, (B, H, C)),
+        kda = c.kind == R.RSSM_KIND_KDA
+        out = {"alpha": view(off[0], B * H * C * N, (B, H, C, N)) if kda else view(off[0], B * H * C, (B, H, C)),
                "v": view(off[2], B * H * C * P, (B, H, C, P)),
                "k": view(off[3], B * G * C * N, (B, G, C, N)),
                "q": view(off[4], B * G * C * N, (B, G, C, N))}
-        out["beta"] = view(off[1], B * H * C, (B, H, C)) if c.kind == R.RSSM_KIND_GDN else None
+        out["beta"] = view(off[1], B * H * C, (B, H, C)) if c.kind != R.RSSM_KIND_MAMBA2 else None
         return out
 
     def read_copy(self):

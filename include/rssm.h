@@ -66,7 +66,7 @@ enum {
                                       draft; sequence untouched */
 };
 
-enum { RSSM_KIND_MAMBA2 = 0, RSSM_KIND_GDN = 1 };
+enum { RSSM_KIND_MAMBA2 = 0, RSSM_KIND_GDN = 1, RSSM_KIND_KDA = 2 };
 enum { RSSM_DTYPE_F32 = 0, RSSM_DTYPE_BF16 = 1 };
 enum { RSSM_READ_NONE = 0, RSSM_READ_FP8 = 1, RSSM_READ_MXFP4 = 2 };
 
@@ -74,6 +74,11 @@ enum { RSSM_READ_NONE = 0, RSSM_READ_FP8 = 1, RSSM_READ_MXFP4 = 2 };
  *   kind       RSSM_KIND_MAMBA2: S <- a S + v k^T, y = S q (page 4, "What shipped").
  *              RSSM_KIND_GDN: gated delta rule S <- a S (I - b k k^T) + b v k^T,
  *              o = S q (the pages name it without a formula; published form).
+ *              RSSM_KIND_KDA: Kimi Delta Attention, the gated delta rule with one gate
+ *              per key channel, S <- S Diag(a) (I - b k k^T) + b v k^T, o = S q; alpha
+ *              is a dk-vector per value head (page 4 "Why it matters": the replay
+ *              reframing carries over to KDA's delta-rule update; no formula on the
+ *              pages, so the form of KDA's own publication).
  *   batch      B >= 0 sequences.
  *   n_heads    H value heads; n_qk_heads G key/query heads, H % G == 0.
  *   dv, dk     P rows and N columns of a state tile.  dk in {32, 64, 128, 256};
@@ -81,9 +86,9 @@ enum { RSSM_READ_NONE = 0, RSSM_READ_FP8 = 1, RSSM_READ_MXFP4 = 2 };
  *   L          flush threshold (window length; the pages use 16), L >= 1.
  *   t_max      maximum drafts per verify (1 = decode only), 1 <= t_max <= 8.
  *   capacity   ring slots C, L + t_max - 1 <= C <= 32.
- *              Each ring region (B*H*C*dv and B*G*C*dk elements) and each step
- *              input (B*t_max*H*dv, B*t_max*G*dk elements) holds fewer than 2^31
- *              elements (RSSM_E_SHAPE otherwise).
+ *              Each ring region (B*H*C*dv and B*G*C*dk elements; KDA alpha B*H*C*dk)
+ *              and each step input (B*t_max*H*dv, B*t_max*G*dk elements; KDA alpha
+ *              B*t_max*H*dk) holds fewer than 2^31 elements (RSSM_E_SHAPE otherwise).
  *   in_dtype   RSSM_DTYPE_F32 or RSSM_DTYPE_BF16 for alpha, beta, v, k, q and the ring.
  *   read_copy  RSSM_READ_NONE, RSSM_READ_FP8 (OCP E4M3FN codes + one fp32 scale
  *              amax/448 per 32 elements along dk) or RSSM_READ_MXFP4 (OCP MX
@@ -114,7 +119,8 @@ typedef struct {
  *                 NULL when read_copy == RSSM_READ_NONE.
  *   ring          one buffer holding, at 256-byte aligned offsets in this order
  *                 (element = in_dtype):
- *                   alpha [B][H][C], beta [B][H][C] (GDN only, else absent),
+ *                   alpha [B][H][C] (KDA: [B][H][C][dk]),
+ *                   beta [B][H][C] (GDN and KDA, else absent),
  *                   v [B][H][C][dv], k [B][G][C][dk], q [B][G][C][dk].
  *                 Record of cursor position pos lives in slot pos % C.  Stored
  *                 bits are exact copies of the appended inputs.
@@ -161,12 +167,14 @@ int rssm_init_state(const rssm_config *cfg, const rssm_state *st, const float *s
                     hipStream_t stream);
 
 /* One decode step for every sequence (page 4 "What shipped"; page 1, what the
- * method does).  Inputs: alpha [B][H], beta [B][H] (GDN; NULL for Mamba-2),
+ * method does).  Inputs: alpha [B][H] (KDA: [B][H][dk]), beta [B][H] (GDN and KDA;
+ * NULL for Mamba-2),
  * v [B][H][dv], k [B][G][dk], q [B][G][dk].  Output y [B][H][dv] fp32.
  * Per sequence with h = n_committed - n_ckpt live records before the step:
  *   - if h + 1 < L: append the record at slot n_committed % C and write
  *     y = G S_read q + sum_j decay(j -> now) (k_j . q) v_j (Mamba-2; GDN uses the
- *     equivalent query-transform form) where S_read is S_ckpt or its read copy;
+ *     equivalent query-transform form; KDA the same form with the per-channel gates
+ *     applied to the transformed query) where S_read is S_ckpt or its read copy;
  *     S_ckpt is not written;
  *   - else (flush step): fold the h ring records and the current one into
  *     S_ckpt, write it (and the read copy) once, set n_ckpt = n_committed + 1;
@@ -190,7 +198,8 @@ int rssm_flush(const rssm_config *cfg, const rssm_state *st, int32_t min_records
  *   Mamba-2: O[:, tau] = G_{h+tau} S_ckpt q_tau + sum_{j <= h+tau} W[j, tau] (k_j . q_tau) v_j
  *   GDN:     the same with pseudo-values from the delta rule's triangular system,
  *            evaluated per draft in query-transform form.
- * Draft inputs: alpha [B][T][H], beta [B][T][H] (GDN), v [B][T][H][dv],
+ *   KDA:     per draft, the query-transform form with per-channel gates.
+ * Draft inputs: alpha [B][T][H] (KDA: [B][T][H][dk]), beta [B][T][H] (GDN, KDA), v [B][T][H][dv],
  * k [B][T][G][dk], q [B][T][G][dk].  S_ckpt is never written.  A sequence with
  * h + T > C sets RSSM_DEVERR_VERIFY_CAPACITY and is left untouched (no ring
  * write, its O rows not written). */

@@ -81,24 +81,30 @@ SHAPES = [
     ("gdn", "bf16", 2, 2, 2, 33, 32, 3, 3),
     ("mamba2", "bf16", 2, 3, 3, 64, 128, 32, 32),   # longest window: records staged in two rounds
     ("gdn", "bf16", 2, 2, 1, 128, 128, 32, 32),
+    ("kda", "bf16", 3, 4, 2, 40, 64, 6, 6),
+    ("kda", "fp32", 2, 2, 2, 128, 128, 16, 16),
+    ("kda", "bf16", 2, 2, 2, 33, 32, 3, 3),         # rows not 16-byte aligned: element-wise staging
+    ("kda", "bf16", 2, 2, 1, 128, 128, 32, 32),
 ]
+
+_BASE = {"mamba2": "m2_tiny", "gdn": "gdn_b256", "kda": "kda_b256"}
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_decode_shapes_and_ragged_tails(shape):
     kind, dt, B, H, G, P, N, L, C = shape
-    base = get_workload("gdn_b256" if kind == "gdn" else "m2_tiny")
+    base = get_workload(_BASE[kind])
     wl = base.replace(name="shape", batch=B, n_heads=H, n_qk_heads=G, dv=P, dk=N, in_dtype=dt, L=L,
                       t_max=1, capacity=C, read_copy="none")
     _run_small(wl, 3 * L + 3)
 
 
-@pytest.mark.parametrize("kind,L", [("mamba2", 4), ("mamba2", 16), ("gdn", 8)])
+@pytest.mark.parametrize("kind,L", [("mamba2", 4), ("mamba2", 16), ("gdn", 8), ("kda", 8)])
 def test_staggered_windows_decode(kind, L):
     """Windows at different phases: sequence b first commits b mod L one-draft verifies
     (verify(T=1) + commit(0 or 1)), so each decode step folds only the sequences whose window
     fills on that step.  Every output, cursor and checkpoint against the oracle for 2L steps."""
-    base = get_workload("gdn_b256" if kind == "gdn" else "m2_tiny")
+    base = get_workload(_BASE[kind])
     wl = base.replace(name="stagger", batch=2 * L + 1, n_heads=3 if kind == "mamba2" else 4,
                       n_qk_heads=3 if kind == "mamba2" else 2, dv=24, dk=64, in_dtype="bf16", L=L, t_max=1,
                       capacity=L, read_copy="none")
@@ -135,9 +141,9 @@ def test_staggered_windows_decode(kind, L):
 
 
 def test_conventional_comparator_small():
-    for name in ("m2_tiny", "gdn_b256"):
+    for name in ("m2_tiny", "gdn_b256", "kda_b256"):
         wl = get_workload(name)
-        if name == "gdn_b256":
+        if name != "m2_tiny":
             wl = wl.replace(batch=3, n_heads=4, n_qk_heads=2, dv=24, dk=32, in_dtype="fp32")
         seqs = list(range(wl.batch))
         S0 = initial_state(wl, seqs)

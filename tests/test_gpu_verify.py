@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 def _small(name, **kw):
     wl = get_workload(name)
-    if name.startswith("gdn"):
+    if name.startswith(("gdn", "kda")):
         base = dict(batch=6, n_heads=4, n_qk_heads=2, dv=48, dk=64)
     else:
         base = dict(batch=6, n_heads=4, n_qk_heads=4, dv=20, dk=32)
@@ -50,7 +50,7 @@ def _poison_rejected(ds, nc_before, acc, T):
                 ring["beta"][b, :, slot] = nan
 
 
-@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_spec_small(name, dtype):
     """A few decode steps, then verify(T) / commit(a) / flush(L): outputs, cursors, checkpoints."""
@@ -89,7 +89,7 @@ def test_spec_small(name, dtype):
     assert ds.error() == 0
 
 
-@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256", "kda_b256"])
 def test_rejected_slots_are_never_read(name):
     """Poisoning every rejected draft slot with NaN changes no output and no checkpoint bit."""
     wl = _small(name)
@@ -199,15 +199,16 @@ def test_serving_shape_verify_sampled():
     assert ds.error() == 0
 
 
-def test_serving_shape_gdn_decode_then_verify_sampled():
-    """Gated DeltaNet at B=256, 32 value / 16 key heads, 128 x 128 tiles: 256 decode steps,
-    then 256 verify steps with T = 4 drafts."""
-    wl = get_workload("gdn_b256")
+@pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
+def test_serving_shape_gdn_decode_then_verify_sampled(name):
+    """Gated DeltaNet at B=256, 32 value / 16 key heads, 128 x 128 tiles (KDA: 32 heads with
+    per-channel gates): 256 decode steps, then 256 verify steps with T = 4 drafts."""
+    wl = get_workload(name)
     T = wl.t_max
     nd, nv = wl.decode_steps, wl.verify_steps
     seqs = list(range(wl.batch))
     sample = [0, 128, 255]
-    print(f"[serving gdn] oracle runs for {sample}", flush=True)
+    print(f"[serving {name}] oracle runs for {sample}", flush=True)
     ref = spec_runs(wl, sample, nd, nv, T, ckpt_every=64)
     cur = cursor_run(wl, nv, verify=True, T=T, decode_steps=nd)
     ds = new_state(wl, initial_state(wl, seqs))
@@ -221,7 +222,7 @@ def test_serving_shape_gdn_decode_then_verify_sampled():
             got = y[idx].cpu().numpy()
             for i, b in enumerate(sample):
                 worst_d = max(worst_d, relerr(got[i], ref[b]["y"][t]).max())
-        print(f"[serving gdn] decode worst rel err {worst_d:.3g}", flush=True)
+        print(f"[serving {name}] decode worst rel err {worst_d:.3g}", flush=True)
         for s in range(nv):
             verify(ds, T, to_dev_inputs(src.drafts(s, T)), o)
             got = o[idx].cpu().numpy()
@@ -235,12 +236,12 @@ def test_serving_shape_gdn_decode_then_verify_sampled():
                     e = tile_relerr(ds.ckpt()[b].cpu().numpy(), ref[b]["ckpt"][s]).max()
                     assert e <= TOL, f"step {s} seq {b}: checkpoint rel err {e:.3g}"
             if s % 64 == 63:
-                print(f"[serving gdn] verify step {s + 1}/{nv} worst rel err {worst_v:.3g}", flush=True)
+                print(f"[serving {name}] verify step {s + 1}/{nv} worst rel err {worst_v:.3g}", flush=True)
     assert worst_d <= TOL and worst_v <= TOL
     assert ds.error() == 0
 
 
-@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_snapshot_verify_small(name, dtype):
     """The snapshot-based speculative comparator: outputs of every draft against the oracle's
@@ -335,7 +336,7 @@ def _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=True):
         assert e <= TOL, f"step {s}: checkpoint rel err {e:.3g}"
 
 
-@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_tree_spec_small(name, dtype):
     """Tree-shaped drafts: verify_tree -> commit_tree(path) -> flush(L) against the oracle:
@@ -355,7 +356,7 @@ def test_tree_spec_small(name, dtype):
 def test_chain_tree_matches_linear_verify_bits():
     """A tree in which every draft hangs off the previous one is the linear chain: the
     outputs are bit-identical to rssm_verify's."""
-    for name in ("m2_verify_b512", "gdn_b256"):
+    for name in ("m2_verify_b512", "gdn_b256", "kda_b256"):
         wl = _small(name)
         T = wl.t_max
         seqs = list(range(wl.batch))
@@ -480,7 +481,7 @@ def _fused_loop(wl, steps, tree, seed0=400):
     return full
 
 
-@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256"])
+@pytest.mark.parametrize("name", ["m2_verify_b512", "gdn_b256", "kda_b256"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("tree", [False, True])
 def test_verify_with_fused_flush(name, dtype, tree):
