@@ -982,6 +982,8 @@ __device__ __forceinline__ void fold_gdn(Frag<N, RGW> &F, const float *lds, cons
 
 // KDA fold, one per-channel gated delta-rule update per record in registers:
 // S <- S Diag(a) ; u = b (v - S k) ; S <- S + u k^T (a: the record's alpha row in LDS).
+// The gate is applied in place in the first pass, so only the key row stays live into the
+// rank-1 pass (the gate row is dead after it).
 template <int N, int RGW>
 __device__ __forceinline__ void fold_kda(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P,
                                          int wave, int lane) {
@@ -996,9 +998,14 @@ __device__ __forceinline__ void fold_kda(Frag<N, RGW> &F, const float *lds, cons
 #pragma unroll
     for (int f = 0; f < N / 32; ++f) {
       const float4 kf = *(const float4 *)(kr + 32 * f), af = *(const float4 *)(ar + 32 * f);
-      const float4 akf = make_float4(af.x * kf.x, af.y * kf.y, af.z * kf.z, af.w * kf.w);
 #pragma unroll
-      for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], akf, w[i]);
+      for (int i = 0; i < RGW; ++i) {
+        F.s[i][f].x *= af.x;
+        F.s[i][f].y *= af.y;
+        F.s[i][f].z *= af.z;
+        F.s[i][f].w *= af.w;
+        w[i] = dot4(F.s[i][f], kf, w[i]);
+      }
     }
     float u[RGW];
 #pragma unroll
@@ -1010,13 +1017,13 @@ __device__ __forceinline__ void fold_kda(Frag<N, RGW> &F, const float *lds, cons
     }
 #pragma unroll
     for (int f = 0; f < N / 32; ++f) {
-      const float4 kf = *(const float4 *)(kr + 32 * f), af = *(const float4 *)(ar + 32 * f);
+      const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
       for (int i = 0; i < RGW; ++i) {
-        F.s[i][f].x = fmaf(af.x, F.s[i][f].x, u[i] * kf.x);
-        F.s[i][f].y = fmaf(af.y, F.s[i][f].y, u[i] * kf.y);
-        F.s[i][f].z = fmaf(af.z, F.s[i][f].z, u[i] * kf.z);
-        F.s[i][f].w = fmaf(af.w, F.s[i][f].w, u[i] * kf.w);
+        F.s[i][f].x = fmaf(u[i], kf.x, F.s[i][f].x);
+        F.s[i][f].y = fmaf(u[i], kf.y, F.s[i][f].y);
+        F.s[i][f].z = fmaf(u[i], kf.z, F.s[i][f].z);
+        F.s[i][f].w = fmaf(u[i], kf.w, F.s[i][f].w);
       }
     }
   }

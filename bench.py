@@ -14,6 +14,8 @@ Other measurements of the path (--workload):
   m2_readcopy_b256  Mamba-2 replay decode with an fp8 or MXFP4 read copy (--read-copy)
   m2_verify_b512    speculative verify(T=4) -> commit -> flush(16), B=512 (Mamba-2)
   gdn_verify_b256   the same loop for Gated DeltaNet, B=256
+  kda_b256          KDA replay decode (per-channel gates), B=256, 32 heads, 128 x 128
+  kda_verify_b256   the speculative loop for KDA, B=256
   --drift           read-copy output drift against the fp32 path over 4096 decode steps
   --sweep-L         window length L in {4, 8, 16, 32}, flushes in lockstep and staggered
   --snapshot        with a verify workload: the snapshot-based speculative comparator
@@ -59,9 +61,11 @@ def _es(wl) -> int:
 
 
 def _rec_bytes(wl):
-    """(bytes of one record per value head: alpha (+beta) + v, per key head: k)."""
+    """(bytes of one record per value head: alpha (KDA: dk gates) (+beta) + v, per key head: k)."""
     s = _es(wl)
-    return s * (1 + wl.dv + (1 if wl.kind == "gdn" else 0)), s * wl.dk
+    n_alpha = wl.dk if wl.kind == "kda" else 1
+    n_beta = 0 if wl.kind == "mamba2" else 1
+    return s * (n_alpha + wl.dv + n_beta), s * wl.dk
 
 
 def _tile_read_bytes(wl, fold: bool) -> int:
@@ -801,7 +805,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="layer instances used round robin (decode workloads)")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions of K steps; the median is reported")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=[WORKLOAD, "gdn_b256", "m2_readcopy_b256", "m2_verify_b512", "gdn_verify_b256"])
+                    choices=[WORKLOAD, "gdn_b256", "kda_b256", "m2_readcopy_b256", "m2_verify_b512",
+                             "gdn_verify_b256", "kda_verify_b256"])
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
     ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
     ap.add_argument("--tree", action="store_true", help="verify workloads: tree-shaped drafts (verify_tree/commit_tree)")
@@ -848,8 +853,9 @@ def main():
             res["cpu_baseline"] = None
         print(json.dumps(res))
         return
-    if args.workload in ("m2_verify_b512", "gdn_verify_b256"):
-        wl = get_workload("m2_verify_b512" if args.workload == "m2_verify_b512" else "gdn_b256")
+    if args.workload in ("m2_verify_b512", "gdn_verify_b256", "kda_verify_b256"):
+        wl = get_workload({"m2_verify_b512": "m2_verify_b512", "gdn_verify_b256": "gdn_b256",
+                           "kda_verify_b256": "kda_b256"}[args.workload])
         res = (run_verify_snapshot(args, wl) if args.snapshot
                else run_verify(args, wl, tree=args.tree, fused=args.fused))
     else:
