@@ -145,7 +145,12 @@ __device__ __forceinline__ void frag_store(const Frag<N, RGW> &F, float *__restr
     if (row < P) {
       float4 *dst = (float4 *)(tile + (int64_t)row * N + c);
 #pragma unroll
-      for (int f = 0; f < N / 32; ++f) dst[8 * f] = F.s[i][f];
+      for (int f = 0; f < N / 32; ++f) {
+        const float4 x = F.s[i][f];
+        f4v v;
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        __builtin_nontemporal_store(v, (f4v *)(dst + 8 * f));
+      }
     }
   }
 }
@@ -771,98 +776,24 @@ __device__ void kq_dots(float *lds, const LdsLayout &L, int cap, int nrec, int T
   }
 }
 
-// Gated DeltaNet: Gram matrix K^T K (i < m) and K^T q_tau for T queries over nrec records.
-// Pair p of the Gram part is (i, m) with m (m - 1) / 2 <= p < m (m + 1) / 2, i = p - m (m - 1) / 2.
-template <int N>
-__device__ void gram_and_kq(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
-  const int g16 = t >> 4, l16 = t & 15;
-  const int nkq = T * nrec;
-  const int nd = nkq + nrec * (nrec - 1) / 2;
-  const float inv = 1.0f / (float)nrec;
-  for (int d = g16; d < nd; d += kThreads / 16) {
-    const float *A, *Bv;
-    int i, m = 0, tau = 0;
-    if (d < nkq) {
-      tau = small_div(d, inv);
-      i = d - tau * nrec;
-      A = lds + L.K + i * (N + 4);
-      Bv = lds + L.q + tau * N;
-    } else {
-      const int pp = d - nkq;
-      m = (int)((1.f + sqrtf(8.f * (float)pp + 1.f)) * 0.5f);
-      if (m * (m - 1) / 2 > pp) --m;
-      if (m * (m + 1) / 2 <= pp) ++m;
-      i = pp - (m * (m - 1)) / 2;
-      A = lds + L.K + i * (N + 4);
-      Bv = lds + L.K + m * (N + 4);
-    }
-    const float acc = group_dot<N>(A, Bv, l16);
-    if (l16 == 0) {
-      if (d < nkq)
-        lds[L.coef + tau * cap + i] = acc;            // k_i . q_tau, replaced by e after the solve
-      else
-        lds[L.gram + i * (cap + 1) + m] = acc;        // k_i . k_m, i < m
-    }
-  }
-}
-
-// Query-transform solve for one query over records 0..n-1 (one wave; n <= 64):
-// c_i = k_i . q - sum_{m > i} b_m c_m (k_i . k_m); writes b_i c_i (cc row), e_i = d_i b_i c_i
-// (coef row, replacing k_i . q) with d_i = prod_{i < m < n} alpha_m, and G.
-// Off-path records (see on_path) enter with beta = 0 and alpha = 1, so their cc and coef
-// entries are zero.
-__device__ void gdn_solve_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
-                               int hb = 1 << 30, uint32_t anc = 0) {
-  const float *alpha = lds + L.alpha;
-  const float *beta = lds + L.beta;
-  const float *gram = lds + L.gram;
-  float *coef = lds + L.coef + tau * cap;
-  float *cc = lds + L.cc + tau * cap;
-  const bool on = lane < n && on_path(lane, hb, anc);
-  const float bl = on ? beta[lane] : 0.f;
-  float x = (lane < n) ? coef[lane] : 0.f;
-  for (int m = n - 1; m >= 0; --m) {
-    const float bcm = lane_value(bl * x, m);        // b_m c_m (c_m is final at step m)
-    if (lane < m) x = fmaf(-bcm, gram[lane * (cap + 1) + m], x);
-  }
-  float p = on ? alpha[lane] : 1.f;
-  p = wave_suffix_product(p, lane);
-  const float d = __shfl_down(p, 1);
-  if (lane < n) {
-    const float bc = bl * x;
-    cc[lane] = bc;
-    coef[lane] = (lane == n - 1 ? 1.f : d) * bc;
-  }
-  if (lane == 0) lds[L.gam + tau] = p;
-}
-
-// r = q - sum_{i < n} b_i c_i k_i for query tau (threads stride over N); the cc row holds
-// b_i c_i, zero for records off the query's path.
-template <int N>
-__device__ void gdn_transform_query(float *lds, const LdsLayout &L, int cap, int n, int tau, int t0, int stride) {
-  const float *bc = lds + L.cc + tau * cap;
-  for (int e = t0; e < N; e += stride) {
-    float r = lds[L.q + tau * N + e];
-    for (int i = 0; i < n; ++i) r = fmaf(-bc[i], lds[L.K + i * (N + 4) + e], r);
-    lds[L.r + tau * N + e] = r;
-  }
-}
-
 // Sum over the 64 lanes of a wave (all lanes active); every lane gets the same value.
 __device__ __forceinline__ float wave_sum(float v) {
   v = sum16(v);
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
-// KDA query transform for one query over records 0..n-1 (one wave, all lanes active).
-// With the per-channel gate a_i, S_i r = S_{i-1} Diag(a_i) (r - b_i (k_i . r) k_i)
-// + b_i (k_i . r) v_i, so from the newest record down: c_i = b_i (k_i . r),
-// r <- a_i o (r - c_i k_i).  Writes c_i to the coef row (0 for records off the query's
-// path, which act as neutral records), the final r to the r row, and G = 1 (the decays
-// are carried by r).  Lane l holds elements l + 64 e.
-template <int N>
-__device__ void kda_sweep_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
-                               int hb = 1 << 30, uint32_t anc = 0) {
+// Delta-rule query transform for one query over records 0..n-1 (one wave, all lanes
+// active), the output-only form of Gated DeltaNet and KDA.  With the gate a_i (a scalar for
+// Gated DeltaNet, one per key channel for KDA), S_i r = S_{i-1} Diag(a_i) (r - b_i (k_i . r)
+// k_i) + b_i (k_i . r) v_i, so from the newest record down: c_i = b_i (k_i . r),
+// r <- a_i o (r - c_i k_i), and the output is S_ckpt r + sum_i c_i v_i.  This is the
+// triangular system of the delta rule's pseudo-values solved for one query, evaluated in
+// key space: one wave-wide dot product and one gated AXPY per record.  Writes c_i to the
+// coef row (0 for records off the query's path, which act as neutral records), the final r
+// to the r row, and G = 1 (the decays are carried by r).  Lane l holds elements l + 64 e.
+template <int KIND, int N>
+__device__ void delta_sweep_wave(float *lds, const LdsLayout &L, int cap, int n, int tau, int lane,
+                                 int hb = 1 << 30, uint32_t anc = 0) {
   constexpr int E = (N + 63) / 64;
   const float *beta = lds + L.beta;
   float *coef = lds + L.coef + tau * cap;
@@ -878,7 +809,7 @@ __device__ void kda_sweep_wave(float *lds, const LdsLayout &L, int cap, int n, i
       continue;
     }
     const float *k = lds + L.K + i * (N + 4);
-    const float *al = lds + L.alpha + i * (N + 4);
+    const float *al = lds + L.alpha + (KIND == RSSM_KIND_KDA ? i * (N + 4) : i);
     float p = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -889,7 +820,7 @@ __device__ void kda_sweep_wave(float *lds, const LdsLayout &L, int cap, int n, i
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int idx = lane + 64 * e;
-      if (idx < N) r[e] = al[idx] * fmaf(-c, k[idx], r[e]);
+      if (idx < N) r[e] = (KIND == RSSM_KIND_KDA ? al[idx] : al[0]) * fmaf(-c, k[idx], r[e]);
     }
     if (lane == 0) coef[i] = c;
   }
@@ -1134,16 +1065,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(Args a) {
       __syncthreads();
       x = lds + L.q;
       dec = lds + L.dec;
-    } else if (KIND == RSSM_KIND_KDA) {
-      if (wave == 0) kda_sweep_wave<N>(lds, L, cap, nrec, 0, lane);
-      __syncthreads();
-      x = lds + L.r;
     } else {
-      gram_and_kq<N>(lds, L, cap, nrec, 1, t);
-      __syncthreads();
-      if (wave == 0) gdn_solve_wave(lds, L, cap, nrec, 0, lane);
-      __syncthreads();
-      gdn_transform_query<N>(lds, L, cap, nrec, 0, t, kThreads);
+      if (wave == 0) delta_sweep_wave<KIND, N>(lds, L, cap, nrec, 0, lane);
       __syncthreads();
       x = lds + L.r;
     }
@@ -1265,21 +1188,9 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     __syncthreads();
     xbase = lds + Lv.q;
     dec = lds + Lv.dec;
-  } else if (KIND == RSSM_KIND_KDA) {
-    for (int tau = wave; tau < T; tau += kWaves)
-      kda_sweep_wave<N>(lds, Lv, cap, hv + tau + 1, tau, lane, hv, anc[tau]);
-    __syncthreads();
-    xbase = lds + Lv.r;
   } else {
-    gram_and_kq<N>(lds, Lv, cap, hv + T, T, t);
-    __syncthreads();
     for (int tau = wave; tau < T; tau += kWaves)
-      gdn_solve_wave(lds, Lv, cap, hv + tau + 1, tau, lane, hv, anc[tau]);
-    __syncthreads();
-    for (int e = t; e < T * N; e += kThreads) {
-      const int tau = e / N;
-      gdn_transform_query<N>(lds, Lv, cap, hv + tau + 1, tau, e - tau * N, N);
-    }
+      delta_sweep_wave<KIND, N>(lds, Lv, cap, hv + tau + 1, tau, lane, hv, anc[tau]);
     __syncthreads();
     xbase = lds + Lv.r;
   }

@@ -57,7 +57,7 @@ struct Args {
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
 // Rows of N floats (K, KDA's alpha) are padded by 4 floats.
 struct LdsLayout {
-  int alpha, beta, dec, coef, cc, gam, misc, anc, q, r, K, V, gram, total;
+  int alpha, beta, dec, coef, gam, misc, anc, q, r, K, V, total;
 };
 
 __host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
@@ -69,7 +69,6 @@ __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P,
   l.beta = o;  o += up4(cap);
   l.dec = o;   o += up4(T * cap);
   l.coef = o;  o += up4(T * cap);
-  l.cc = o;    o += up4(T * cap);
   l.gam = o;   o += up4(T);
   l.misc = o;  o += 4;
   l.anc = o;   o += up4(2 * T);     // verify: draft parents and ancestor masks (int32)
@@ -77,7 +76,6 @@ __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P,
   l.r = o;     o += T * N;
   l.K = o;     o += cap * (N + 4);
   l.V = o;     o += up4(cap * P);
-  l.gram = o;  o += (kind == RSSM_KIND_GDN) ? up4(cap * (cap + 1)) : 0;
   l.total = o;
   return l;
 }
