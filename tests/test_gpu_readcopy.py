@@ -144,3 +144,38 @@ def test_serving_shape_read_copy_sampled(fmt):
     if fmt == "fp8":
         assert worst <= TOL_READ
     assert ds.error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_delta_rule_decode_with_read_copy(kind, fmt):
+    """Gated DeltaNet and KDA decode with a read copy: non-flush outputs come from the copy
+    through the delta-rule sweep.  Each output within 5e-2 (normwise) of the oracle, which
+    quantises its own fp32 checkpoint and steps a chain restarted from the dequantised copy
+    (the difference left is fp32 rounding and the odd element at a rounding boundary); flush
+    steps from the fp32 state to the fp32 tolerance; checkpoints bit-identical to a run
+    without the copy."""
+    wl = get_workload("gdn_b256" if kind == "gdn" else "kda_b256").replace(
+        name="rc", batch=3, n_heads=4, n_qk_heads=2, dv=40, dk=64, in_dtype="bf16", L=5, t_max=1,
+        capacity=5, read_copy=fmt)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    plain = new_state(wl.replace(read_copy="none"), S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    for t in range(20):
+        inp = decode_inputs(wl, t, seqs)
+        d = to_dev_inputs(inp)
+        decode(ds, d, y)
+        decode(plain, d, y2)
+        yr = orc.decode(inp)
+        err = relerr(y.cpu().numpy(), yr).max()
+        flush = (t + 1) % wl.L == 0
+        assert err <= (TOL if flush else TOL_READ), f"step {t}: rel err {err:.3g} (flush={flush})"
+        assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32))
+        if flush:
+            assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+            assert tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max() <= TOL
+    assert ds.error() == 0
