@@ -641,9 +641,10 @@ __device__ __forceinline__ void stage_with_tile(const StageSpec &sp, float *lds,
 // Append record row j of LDS (and query row qr) to ring slot `slot` (values are exact
 // widenings of the inputs, so narrowing back to bf16 reproduces the input bits).  KDA's
 // alpha is an N-vector per value head, stored like a key row.
+// t: the caller's thread index among the nthr threads that share the record's chunks.
 template <int KIND, int N>
 __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *lds, int b, int hh, int gq, int j,
-                                int qr, int slot, int t) {
+                                int qr, int slot, int t, int nthr = kThreads) {
   const Geom &g = a.g;
   const int P = g.P;
   const int hr = (b * g.H + hh) * g.C + slot;
@@ -664,7 +665,7 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
       // each, key-head leader only)
       const int cv = P / 8, ck = N / 8, ca = KIND == RSSM_KIND_KDA ? ck : 0;
       const int total = cv + ca + (lead ? 2 * ck : 0);
-      for (int c = t; c < total; c += kThreads) {
+      for (int c = t; c < total; c += nthr) {
         const float *src;
         uint16_t *dst;
         if (c < cv) {
@@ -689,12 +690,12 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
         *(uint4 *)dst = w;
       }
     } else {
-      for (int p = t; p < P; p += kThreads) rV[hr * P + p] = (uint16_t)(__float_as_uint(lds[L.V + j * P + p]) >> 16);
+      for (int p = t; p < P; p += nthr) rV[hr * P + p] = (uint16_t)(__float_as_uint(lds[L.V + j * P + p]) >> 16);
       if (KIND == RSSM_KIND_KDA)
-        for (int n = t; n < N; n += kThreads)
+        for (int n = t; n < N; n += nthr)
           rA[hr * N + n] = (uint16_t)(__float_as_uint(lds[L.alpha + j * (N + 4) + n]) >> 16);
       if (lead)
-        for (int n = t; n < N; n += kThreads) {
+        for (int n = t; n < N; n += nthr) {
           rK[kr + n] = (uint16_t)(__float_as_uint(lds[L.K + j * (N + 4) + n]) >> 16);
           rQ[kr + n] = (uint16_t)(__float_as_uint(lds[L.q + qr * N + n]) >> 16);
         }
@@ -708,11 +709,11 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
       if (KIND != RSSM_KIND_KDA) rA[hr] = lds[L.alpha + j];
       if (KIND != RSSM_KIND_MAMBA2) ((float *)(a.ring + g.off_beta))[hr] = lds[L.beta + j];
     }
-    for (int p = t; p < P; p += kThreads) rV[hr * P + p] = lds[L.V + j * P + p];
+    for (int p = t; p < P; p += nthr) rV[hr * P + p] = lds[L.V + j * P + p];
     if (KIND == RSSM_KIND_KDA)
-      for (int n = t; n < N; n += kThreads) rA[hr * N + n] = lds[L.alpha + j * (N + 4) + n];
+      for (int n = t; n < N; n += nthr) rA[hr * N + n] = lds[L.alpha + j * (N + 4) + n];
     if (lead)
-      for (int n = t; n < N; n += kThreads) {
+      for (int n = t; n < N; n += nthr) {
         rK[kr + n] = lds[L.K + j * (N + 4) + n];
         rQ[kr + n] = lds[L.q + qr * N + n];
       }
@@ -1149,6 +1150,16 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     anc[t] = m;
   }
   __syncthreads();
+  for (int tau = 0; tau < T; ++tau)
+    if (anc[tau] == 0) {             // an invalid tree: nothing is written for this sequence
+      if (t == 0) atomicOr(a.err, RSSM_DEVERR_TREE);
+      return;
+    }
+  // Draft tau goes to slot (n_committed + tau) mod C, appended now by wave tau % 4 while the
+  // tile loads are in flight.  Draft slots are never a committed record's slot (h + T <= C),
+  // so neither this tile's fold nor a sibling head's staging reads them.
+  for (int tau = wave; tau < T; tau += kWaves)
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), lane, 64);
   if (FOLD && fold) {                // the flush part: fold the hb committed records
     if (KIND == RSSM_KIND_MAMBA2) {
       if (wave == 0) wave_decays(lds + L.alpha, hb - 1, lds + L.dec, lds + L.gam, cap, lane);
@@ -1162,11 +1173,6 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     if (t == 0) a.n_ckpt[tile] = nc;
     __syncthreads();                 // the decay rows are rewritten below
   }
-  for (int tau = 0; tau < T; ++tau)
-    if (anc[tau] == 0) {
-      if (t == 0) atomicOr(a.err, RSSM_DEVERR_TREE);
-      return;
-    }
   // A folded window's records are in the checkpoint now: the verify reads record views that
   // start past them (the drafts only).  Otherwise the views are the staged records.
   const int r0 = fold ? hb : 0;
@@ -1202,9 +1208,6 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dec ? dec + tau * cap : nullptr, lds + Lv.coef + tau * cap,
                     hv + tau + 1, P, orow, wave, lane);
   }
-  // draft tau goes to slot (n_committed + tau) mod C
-  for (int tau = 0; tau < T; ++tau)
-    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), t);
 }
 
 template <int KIND, int N, int RGW, int RCF, int STG>

@@ -223,7 +223,8 @@ int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_a
  * on tau's root-to-node path only: drafts off that path enter the replay form as records
  * with alpha = 1, beta = 0 and no contribution.  Drafts are appended at slots
  * (n_committed + tau) % C as in rssm_verify.  An invalid parent sets RSSM_DEVERR_TREE
- * and leaves the sequence untouched; h + T > C as in rssm_verify. */
+ * and leaves the sequence untouched (with rssm_verify_fold: not folded either); h + T > C
+ * as in rssm_verify. */
 int rssm_verify_tree(const rssm_config *cfg, const rssm_state *st, int32_t T,
                      const int32_t *parent, const void *alpha, const void *beta,
                      const void *v, const void *k, const void *q, float *o, hipStream_t stream);
