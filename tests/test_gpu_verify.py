@@ -416,6 +416,40 @@ def test_tree_contract_errors():
     assert nc[:, 0].tolist() == [2, 0, 0, 0, 0, 0]
 
 
+def test_invalid_tree_in_fused_verify_leaves_sequence_untouched():
+    """verify_fold with an invalid draft tree: that sequence is neither folded nor appended
+    (checkpoint bits, n_ckpt and ring unchanged), RSSM_DEVERR_TREE is set; the other
+    sequences fold and verify as usual."""
+    wl = _small("gdn_b256")
+    wl = wl.replace(capacity=wl.L + 2 * wl.t_max - 1)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    for t in range(3):
+        decode(ds, to_dev_inputs(decode_inputs(wl, t, seqs)), y)
+    ck_before = ds.ckpt().clone()
+    ring_before = {k: (None if v is None else v.clone()) for k, v in ds.ring_arrays().items()}
+    parent = np.tile(np.array([-1, 0, 1, 1], np.int32), (wl.batch, 1))
+    parent[2, 3] = 3                                   # not an earlier draft
+    par_d = dev(parent)
+    d = to_dev_inputs(draft_inputs(wl, 0, seqs, T))
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    R.rssm_verify_fold(ds.cfg, ds.st, 3, T, ptr(par_d), ptr(d["alpha"]), ptr(d["beta"]), ptr(d["v"]),
+                       ptr(d["k"]), ptr(d["q"]), ptr(o), stream())
+    assert ds.error() == R.RSSM_DEVERR_TREE
+    nc, nk = counters(ds)
+    assert nk[2].tolist() == [0] * wl.n_heads and nc[2].tolist() == [3] * wl.n_heads
+    assert torch.equal(ds.ckpt()[2].view(torch.int32), ck_before[2].view(torch.int32))
+    ring_after = ds.ring_arrays()
+    for f in ("alpha", "beta", "v"):
+        assert torch.equal(ring_before[f][2], ring_after[f][2]), f
+    others = [b for b in seqs if b != 2]
+    assert all(nk[b].tolist() == [3] * wl.n_heads for b in others)
+    assert not torch.equal(ds.ckpt()[0].view(torch.int32), ck_before[0].view(torch.int32))
+
+
 def test_tree_spec_full_heads():
     """Tree speculation at the serving head shape (H=128, P=64, N=128, bf16, C=19) for a
     batch of 12 sequences, 40 steps: every output, cursor and checkpoint."""
