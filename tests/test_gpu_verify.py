@@ -563,3 +563,43 @@ def test_verify_fold_capacity_rule():
     assert np.array_equal(nc0, nc1) and np.array_equal(nk0, nk1)
     assert torch.equal(ck0, ds.ckpt())
     assert not o.any()
+
+
+MAX_SHAPES = [
+    # name, dv, dk: T = 8 drafts (the maximum) and C = 32 ring slots (the maximum), L = C - T + 1
+    ("m2_verify_b512", 64, 256),
+    ("gdn_b256", 128, 128),
+    ("kda_b256", 64, 128),
+]
+
+
+@pytest.mark.parametrize("shape", MAX_SHAPES, ids=lambda s: f"{s[0]}-{s[1]}x{s[2]}")
+def test_spec_at_maximum_drafts_and_capacity(shape):
+    """The largest draft count (8) and ring (32 slots) the ABI allows, at the widest tiles the
+    LDS budget admits: linear verify -> commit -> flush(L), then tree verify -> commit_tree ->
+    flush(L), then the flush fused into the verify, each against the oracle."""
+    name, P, N = shape
+    wl = _small(name, batch=3, dv=P, dk=N, t_max=8, capacity=32, L=25)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(12):
+        d = draft_inputs(wl, s, seqs, T)
+        verify(ds, T, to_dev_inputs(d), o)
+        err = relerr(o.cpu().numpy(), orc.verify(d, T)).max()
+        assert err <= TOL, f"verify step {s}: rel err {err:.3g}"
+        acc = accept_counts(wl, s, T)[: wl.batch]
+        _commit(ds, dev(acc), T)
+        orc.commit(acc, T)
+        _flush(ds, wl.L)
+        orc.flush(wl.L)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {s}")
+        e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
+        assert e <= TOL, f"step {s}: checkpoint rel err {e:.3g}"
+    for s in range(12):
+        _tree_step(ds, orc, wl, 100 + s, T, seqs, o)
+    assert ds.error() == 0
+    _fused_loop(wl.replace(capacity=32, L=32 - 2 * T + 1), 12, tree=False)
