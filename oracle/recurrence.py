@@ -24,6 +24,11 @@ replaced by a per-key-channel gate a_t in (0, 1]^N,
 in this [P][N] orientation (rows: value dim, columns: key dim), again evaluated
 as decay, error against the decayed state, rank-1 write.  The gate is per value
 head: alpha has shape [H, N].
+
+Parity unpinned: that the Gated DeltaNet and KDA forms above are the ones the
+pages' own kernels compute (the pages give neither formula).  The oracle's
+evaluation of these forms is pinned (tests/test_oracle_pins.py,
+tests/test_oracle_kda.py: Kronecker unrolling, exact rationals, special cases).
 """
 from __future__ import annotations
 
