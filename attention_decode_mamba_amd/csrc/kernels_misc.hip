@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
   const int t = threadIdx.x;
   const int T = a.T;
   const int H = g.H, G = g.G, P = g.P, N = g.N, C = g.C;
+  const size_t BH = (size_t)g.B * H, BG = (size_t)g.B * G;   // rows per ring slot
   const int64_t nc = a.n_committed[(int64_t)b * H], nk = a.n_ckpt[(int64_t)b * H];
   const int64_t hb = nc - nk;
   if (hb < 0 || hb > C) {
@@ -99,9 +100,9 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       for (int f = f0; f < f1; ++f) {
         const int64_t base = f == 0 ? g.off_alpha : g.off_beta;
         if (es == 2)
-          *(uint16_t *)(a.ring + base + (hr * C + dst) * 2) = *(const uint16_t *)(a.ring + base + (hr * C + src) * 2);
+          *(uint16_t *)(a.ring + base + ((size_t)dst * BH + hr) * 2) = *(const uint16_t *)(a.ring + base + ((size_t)src * BH + hr) * 2);
         else
-          *(uint32_t *)(a.ring + base + (hr * C + dst) * 4) = *(const uint32_t *)(a.ring + base + (hr * C + src) * 4);
+          *(uint32_t *)(a.ring + base + ((size_t)dst * BH + hr) * 4) = *(const uint32_t *)(a.ring + base + ((size_t)src * BH + hr) * 4);
       }
     }
     // k and q of every key head: N * es is a multiple of 16 bytes for every dk
@@ -111,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       const int which = row >= G, gg = row - which * G;
       const int64_t base = which ? g.off_q : g.off_k;
       const size_t kr = (size_t)b * G + gg;
-      const uint8_t *ps = a.ring + base + (kr * C + src) * N * es + part * 16;
-      uint8_t *pd = a.ring + base + (kr * C + dst) * N * es + part * 16;
+      const uint8_t *ps = a.ring + base + ((size_t)src * BG + kr) * N * es + part * 16;
+      uint8_t *pd = a.ring + base + ((size_t)dst * BG + kr) * N * es + part * 16;
       *(uint4 *)pd = *(const uint4 *)ps;
     }
     // KDA: the alpha row (dk elements, a whole number of 16-byte chunks) of every value head
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       for (int c = t; c < na; c += kThreads) {
         const int h = c / cpa, part = c - h * cpa;
         const size_t hr = (size_t)b * H + h;
-        const uint8_t *ps = a.ring + g.off_alpha + (hr * C + src) * N * es + part * 16;
-        uint8_t *pd = a.ring + g.off_alpha + (hr * C + dst) * N * es + part * 16;
+        const uint8_t *ps = a.ring + g.off_alpha + ((size_t)src * BH + hr) * N * es + part * 16;
+        uint8_t *pd = a.ring + g.off_alpha + ((size_t)dst * BH + hr) * N * es + part * 16;
         *(uint4 *)pd = *(const uint4 *)ps;
       }
     }
@@ -132,15 +133,15 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       for (int c = t; c < nvc; c += kThreads) {
         const int h = g.cpv_lg >= 0 ? c >> g.cpv_lg : c / cpv, part = c - h * cpv;
         const size_t hr = (size_t)b * H + h;
-        const uint8_t *ps = a.ring + g.off_v + (hr * C + src) * P * es + part * 16;
-        uint8_t *pd = a.ring + g.off_v + (hr * C + dst) * P * es + part * 16;
+        const uint8_t *ps = a.ring + g.off_v + ((size_t)src * BH + hr) * P * es + part * 16;
+        uint8_t *pd = a.ring + g.off_v + ((size_t)dst * BH + hr) * P * es + part * 16;
         *(uint4 *)pd = *(const uint4 *)ps;
       }
     } else {
       for (int e = t; e < H * P; e += kThreads) {
         const int h = e / P, pp = e - h * P;
         const size_t hr = (size_t)b * H + h;
-        const size_t os = g.off_v + ((hr * C + src) * P + pp) * es, od = g.off_v + ((hr * C + dst) * P + pp) * es;
+        const size_t os = g.off_v + (((size_t)src * BH + hr) * P + pp) * es, od = g.off_v + (((size_t)dst * BH + hr) * P + pp) * es;
         if (es == 2)
           *(uint16_t *)(a.ring + od) = *(const uint16_t *)(a.ring + os);
         else

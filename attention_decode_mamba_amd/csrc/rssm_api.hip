@@ -41,15 +41,15 @@ void ring_layout(const rssm_config *c, int64_t off[5], int64_t *total) {
   const int64_t B = c->batch, H = c->n_heads, G = c->n_qk_heads, C = c->capacity;
   const int64_t P = c->dv, N = c->dk;
   int64_t o = 0;
-  off[0] = o;                                   // alpha [B][H][C] (KDA: [B][H][C][N])
+  off[0] = o;                                   // alpha [C][B][H] (KDA: [C][B][H][N])
   o = align256(o + B * H * C * (c->kind == RSSM_KIND_KDA ? N : 1) * es);
-  off[1] = o;                                   // beta [B][H][C] (GDN and KDA)
+  off[1] = o;                                   // beta [C][B][H] (GDN and KDA)
   if (c->kind != RSSM_KIND_MAMBA2) o = align256(o + B * H * C * es);
-  off[2] = o;                                   // v [B][H][C][P]
+  off[2] = o;                                   // v [C][B][H][P]
   o = align256(o + B * H * C * P * es);
-  off[3] = o;                                   // k [B][G][C][N]
+  off[3] = o;                                   // k [C][B][G][N]
   o = align256(o + B * G * C * N * es);
-  off[4] = o;                                   // q [B][G][C][N]
+  off[4] = o;                                   // q [C][B][G][N]
   o = align256(o + B * G * C * N * es);
   *total = o;
 }

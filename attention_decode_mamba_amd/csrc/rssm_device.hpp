@@ -404,7 +404,8 @@ struct StageSpec {
   int cpv_lg;                            // log2 of 16-byte chunks per value row, or -1
   int avec;                              // alpha is an N-vector per record (KDA)
   const uint8_t *rA, *rB, *rV, *rK;      // ring regions
-  int hrow, krow;                        // ring row (slot 0) of this value head / key head
+  int hrow, krow;                        // this value head's / key head's row within a slot
+  int hstr, kstr;                        // rows per slot: B*H value-head rows, B*G key-head rows
   const void *iA, *iB, *iV, *iK, *iQ;    // inputs
   int ia0, ias, iv0, ivs, ik0, iks, iq0, iqs;
   float *A, *Bt, *V, *K, *Q;             // LDS
@@ -453,7 +454,7 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
   if (with_scalars) {
     const int j = t < sp.nrec ? t : sp.nrec - 1;
     const bool ring = j < sp.n_ring;
-    const int ri = sp.hrow + ring_slot(sp, j);
+    const int ri = ring_slot(sp, j) * sp.hstr + sp.hrow;
     const int ii = sp.ia0 + (j - sp.n_ring) * sp.ias;
     if (!AVEC) {
       const uint8_t *pa = ring ? sp.rA + (size_t)ri * es : (const uint8_t *)sp.iA + (size_t)ii * es;
@@ -484,19 +485,19 @@ __device__ __forceinline__ void stage_issue(const StageSpec &sp, StageRegs<U> &R
         const int e = (c - j * cpv) * epc;
         const bool ring = j < sp.n_ring;
         bp = ring ? sp.rV : (const uint8_t *)sp.iV;
-        idx = ring ? (sp.hrow + ring_slot(sp, j)) * sp.P + e : sp.iv0 + (j - sp.n_ring) * sp.ivs + e;
+        idx = ring ? (ring_slot(sp, j) * sp.hstr + sp.hrow) * sp.P + e : sp.iv0 + (j - sp.n_ring) * sp.ivs + e;
         dst = (int)(sp.V - lds) + j * sp.P + e;
       } else if (c < nV + nK) {
         const int l = c - nV, j = l / cpk, e = (l - j * cpk) * epc;
         const bool ring = j < sp.n_ring;
         bp = ring ? sp.rK : (const uint8_t *)sp.iK;
-        idx = ring ? (sp.krow + ring_slot(sp, j)) * sp.N + e : sp.ik0 + (j - sp.n_ring) * sp.iks + e;
+        idx = ring ? (ring_slot(sp, j) * sp.kstr + sp.krow) * sp.N + e : sp.ik0 + (j - sp.n_ring) * sp.iks + e;
         dst = (int)(sp.K - lds) + j * (sp.N + 4) + e;
       } else if (AVEC && c < nV + nK + nA) {
         const int l = c - nV - nK, j = l / cpk, e = (l - j * cpk) * epc;
         const bool ring = j < sp.n_ring;
         bp = ring ? sp.rA : (const uint8_t *)sp.iA;
-        idx = ring ? (sp.hrow + ring_slot(sp, j)) * sp.N + e : (sp.ia0 + (j - sp.n_ring) * sp.ias) * sp.N + e;
+        idx = ring ? (ring_slot(sp, j) * sp.hstr + sp.hrow) * sp.N + e : (sp.ia0 + (j - sp.n_ring) * sp.ias) * sp.N + e;
         dst = (int)(sp.A - lds) + j * (sp.N + 4) + e;
       } else {
         const int l = c - nV - nK - nA, r = l / cpk, e = (l - r * cpk) * epc;
@@ -539,7 +540,7 @@ __device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
   for (int j = t; j < sp.nrec; j += kThreads) {
     float al = 0.f, be = 0.f;
     if (j < sp.n_ring) {
-      const int i = sp.hrow + ring_slot(sp, j);
+      const int i = ring_slot(sp, j) * sp.hstr + sp.hrow;
       if (!sp.avec) al = ld_in(sp.rA, i, sp.bf16);
       if (sp.rB) be = ld_in(sp.rB, i, sp.bf16);
     } else {
@@ -554,17 +555,17 @@ __device__ __forceinline__ void stage_scalar(const StageSpec &sp, int t) {
     for (int e = t; e < sp.nrec * sp.N; e += kThreads) {
       const int j = e / sp.N, n = e - j * sp.N;
       sp.A[j * (sp.N + 4) + n] = j < sp.n_ring
-                                     ? ld_in(sp.rA, (sp.hrow + ring_slot(sp, j)) * sp.N + n, sp.bf16)
+                                     ? ld_in(sp.rA, (ring_slot(sp, j) * sp.hstr + sp.hrow) * sp.N + n, sp.bf16)
                                      : ld_in(sp.iA, (sp.ia0 + (j - sp.n_ring) * sp.ias) * sp.N + n, sp.bf16);
     }
   for (int e = t; e < sp.nrec * sp.P; e += kThreads) {
     const int j = e / sp.P, p = e - j * sp.P;
-    sp.V[e] = j < sp.n_ring ? ld_in(sp.rV, (sp.hrow + ring_slot(sp, j)) * sp.P + p, sp.bf16)
+    sp.V[e] = j < sp.n_ring ? ld_in(sp.rV, (ring_slot(sp, j) * sp.hstr + sp.hrow) * sp.P + p, sp.bf16)
                             : ld_in(sp.iV, sp.iv0 + (j - sp.n_ring) * sp.ivs + p, sp.bf16);
   }
   for (int e = t; e < sp.nrec * sp.N; e += kThreads) {
     const int j = e / sp.N, n = e - j * sp.N;
-    sp.K[j * (sp.N + 4) + n] = j < sp.n_ring ? ld_in(sp.rK, (sp.krow + ring_slot(sp, j)) * sp.N + n, sp.bf16)
+    sp.K[j * (sp.N + 4) + n] = j < sp.n_ring ? ld_in(sp.rK, (ring_slot(sp, j) * sp.kstr + sp.krow) * sp.N + n, sp.bf16)
                                              : ld_in(sp.iK, sp.ik0 + (j - sp.n_ring) * sp.iks + n, sp.bf16);
   }
   for (int e = t; e < sp.nq * sp.N; e += kThreads) {
@@ -593,8 +594,10 @@ __device__ __forceinline__ StageSpec make_spec(const Args &a, const LdsLayout &L
   sp.rB = KIND != RSSM_KIND_MAMBA2 ? a.ring + g.off_beta : nullptr;
   sp.rV = a.ring + g.off_v;
   sp.rK = a.ring + g.off_k;
-  sp.hrow = (b * g.H + hh) * g.C;
-  sp.krow = (b * g.G + gq) * g.C;
+  sp.hrow = b * g.H + hh;
+  sp.krow = b * g.G + gq;
+  sp.hstr = g.B * g.H;
+  sp.kstr = g.B * g.G;
   sp.iA = a.alpha;
   sp.iB = KIND != RSSM_KIND_MAMBA2 ? a.beta : nullptr;
   sp.iV = a.v;
@@ -647,9 +650,9 @@ __device__ void append_from_lds(const Args &a, const LdsLayout &L, const float *
                                 int qr, int slot, int t, int nthr = kThreads) {
   const Geom &g = a.g;
   const int P = g.P;
-  const int hr = (b * g.H + hh) * g.C + slot;
+  const int hr = slot * (g.B * g.H) + (b * g.H + hh);
   const bool lead = (hh % g.grp) == 0;
-  const int kr = ((b * g.G + gq) * g.C + slot) * N;
+  const int kr = (slot * (g.B * g.G) + (b * g.G + gq)) * N;
   if (g.bf16) {
     uint16_t *rA = (uint16_t *)(a.ring + g.off_alpha);
     uint16_t *rV = (uint16_t *)(a.ring + g.off_v);

@@ -61,22 +61,27 @@ class DeviceState:
         return (self.n_committed[: B * H].view(B, H), self.n_ckpt[: B * H].view(B, H))
 
     def ring_arrays(self):
-        """Typed views of the ring regions: alpha [B,H,C] (KDA [B,H,C,N]), beta (GDN, KDA) [B,H,C],
-        v [B,H,C,P], k, q [B,G,C,N]."""
+        """Typed views of the ring regions, indexed [b, head, slot, ...]: alpha [B,H,C] (KDA
+        [B,H,C,N]), beta (GDN, KDA) [B,H,C], v [B,H,C,P], k, q [B,G,C,N].  The ring stores
+        every region slot-major ([C][B][H]...), so these are permuted views of it."""
         c = self.cfg
         off = R.rssm_ring_offsets(c)
         es = 2 if c.in_dtype == R.RSSM_DTYPE_BF16 else 4
         dt = torch.int16 if es == 2 else torch.float32
         B, H, G, C, P, N = c.batch, c.n_heads, c.n_qk_heads, c.capacity, c.dv, c.dk
 
-        def view(o, n, shape):
-            return self.ring[o: o + n * es].view(dt).view(*shape)
+        def view(o, shape):
+            n = 1
+            for d in shape:
+                n *= d
+            t = self.ring[o: o + n * es].view(dt).view(*shape)          # [C][rows][...]
+            return t.permute(1, 2, 0, *range(3, len(shape)))
         kda = c.kind == R.RSSM_KIND_KDA
-        out = {"alpha": view(off[0], B * H * C * N, (B, H, C, N)) if kda else view(off[0], B * H * C, (B, H, C)),
-               "v": view(off[2], B * H * C * P, (B, H, C, P)),
-               "k": view(off[3], B * G * C * N, (B, G, C, N)),
-               "q": view(off[4], B * G * C * N, (B, G, C, N))}
-        out["beta"] = view(off[1], B * H * C, (B, H, C)) if c.kind != R.RSSM_KIND_MAMBA2 else None
+        out = {"alpha": view(off[0], (C, B, H, N)) if kda else view(off[0], (C, B, H)),
+               "v": view(off[2], (C, B, H, P)),
+               "k": view(off[3], (C, B, G, N)),
+               "q": view(off[4], (C, B, G, N))}
+        out["beta"] = view(off[1], (C, B, H)) if c.kind != R.RSSM_KIND_MAMBA2 else None
         return out
 
     def read_copy(self):

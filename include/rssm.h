@@ -118,12 +118,13 @@ typedef struct {
  *   s_read_scale  fp8: fp32 [B][H][dv][dk/32]; MXFP4: E8M0 bytes [B][H][dv][dk/32];
  *                 NULL when read_copy == RSSM_READ_NONE.
  *   ring          one buffer holding, at 256-byte aligned offsets in this order
- *                 (element = in_dtype):
- *                   alpha [B][H][C] (KDA: [B][H][C][dk]),
- *                   beta [B][H][C] (GDN and KDA, else absent),
- *                   v [B][H][C][dv], k [B][G][C][dk], q [B][G][C][dk].
+ *                 (element = in_dtype), each region slot-major:
+ *                   alpha [C][B][H] (KDA: [C][B][H][dk]),
+ *                   beta [C][B][H] (GDN and KDA, else absent),
+ *                   v [C][B][H][dv], k [C][B][G][dk], q [C][B][G][dk].
  *                 Record of cursor position pos lives in slot pos % C.  Stored
- *                 bits are exact copies of the appended inputs.
+ *                 bits are exact copies of the appended inputs.  (Slot-major: the
+ *                 rows one step appends for all sequences are contiguous.)
  *   n_committed   int64 [B][H]: records committed since init (per-tile replicas of
  *                 the per-sequence cursor; all H replicas of a sequence are equal).
  *   n_ckpt        int64 [B][H]: cursor position of the checkpoint.  The ring holds
