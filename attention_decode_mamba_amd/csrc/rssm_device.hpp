@@ -28,11 +28,16 @@ __device__ __forceinline__ float ld_in(const void *base, int64_t i, int bf16) {
   return bf16 ? bf16f(((const uint16_t *)base)[i]) : ((const float *)base)[i];
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous
-// range of tiles so tiles sharing key/query rows (GDN groups) share an L2.
+// Workgroups are dispatched round-robin over the 8 XCDs.  By default each XCD gets a
+// contiguous range of tiles, so tiles sharing key/query rows (GDN groups) share an L2 and
+// the workgroups running at once on an XCD read and append neighbouring rows.  Kernels whose
+// per-sequence cost varies (a flush where only some sequences fold, a verify whose windows
+// differ) take SPREAD: block order = tile order, so a sequence's heads land on all XCDs and
+// the busy sequences do not pile up on a few of them.
+template <bool SPREAD = false>
 __device__ __forceinline__ int tile_of_block(int ntiles) {
   const int bid = blockIdx.x;
-  if ((ntiles & 7) == 0) {
+  if (!SPREAD && (ntiles & 7) == 0) {
     const int per = ntiles >> 3;
     return (bid & 7) * per + (bid >> 3);
   }
@@ -1095,7 +1100,7 @@ template <int KIND, int N, int RGW, bool FOLD, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
-  const int tile = tile_of_block(g.B * g.H);
+  const int tile = tile_of_block<FOLD || KIND != RSSM_KIND_MAMBA2>(g.B * g.H);
   const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int T = a.T;
@@ -1217,7 +1222,7 @@ template <int KIND, int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_flush(Args a) {
   extern __shared__ float lds[];
   const Geom &g = a.g;
-  const int tile = tile_of_block(g.B * g.H);
+  const int tile = tile_of_block<true>(g.B * g.H);
   const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
