@@ -1163,11 +1163,6 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
       if (t == 0) atomicOr(a.err, RSSM_DEVERR_TREE);
       return;
     }
-  // Draft tau goes to slot (n_committed + tau) mod C, appended now by wave tau % 4 while the
-  // tile loads are in flight.  Draft slots are never a committed record's slot (h + T <= C),
-  // so neither this tile's fold nor a sibling head's staging reads them.
-  for (int tau = wave; tau < T; tau += kWaves)
-    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), lane, 64);
   if (FOLD && fold) {                // the flush part: fold the hb committed records
     if (KIND == RSSM_KIND_MAMBA2) {
       if (wave == 0) wave_decays(lds + L.alpha, hb - 1, lds + L.dec, lds + L.gam, cap, lane);
@@ -1216,6 +1211,10 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dec ? dec + tau * cap : nullptr, lds + Lv.coef + tau * cap,
                     hv + tau + 1, P, orow, wave, lane);
   }
+  // Draft tau goes to slot (n_committed + tau) mod C, one wave per draft.  Draft slots are
+  // never a committed record's slot (h + T <= C), so no sibling head's staging reads them.
+  for (int tau = wave; tau < T; tau += kWaves)
+    append_from_lds<KIND, N>(a, L, lds, b, hh, gq, hb + tau, tau, ring_add(sp.slot0, hb + tau, g.C), lane, 64);
 }
 
 template <int KIND, int N, int RGW, int RCF, int STG>
