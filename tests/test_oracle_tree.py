@@ -14,8 +14,8 @@ from synth import accept_counts, draft_inputs, draft_tree, get_workload, initial
 
 
 def _wl(kind, dtype="bf16"):
-    name = "gdn_b256" if kind == "gdn" else "m2_verify_b512"
-    return get_workload(name).replace(name="tree", batch=5, n_heads=4, n_qk_heads=2 if kind == "gdn" else 4,
+    name = {"gdn": "gdn_b256", "kda": "kda_b256"}.get(kind, "m2_verify_b512")
+    return get_workload(name).replace(name="tree", batch=5, n_heads=4, n_qk_heads=2 if kind != "mamba2" else 4,
                                       dv=6, dk=32, in_dtype=dtype)
 
 
@@ -24,7 +24,7 @@ def _pick(drafts, i, order):
     return {k: (None if v is None else v[i:i + 1, order]) for k, v in drafts.items()}
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_chain_tree_is_the_linear_verify(kind):
     wl = _wl(kind)
     T = wl.t_max
@@ -50,7 +50,7 @@ def test_chain_tree_is_the_linear_verify(kind):
     assert not lin.err and not tree.err
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_tree_outputs_follow_root_to_node_paths(kind):
     wl = _wl(kind)
     T = wl.t_max
@@ -74,7 +74,7 @@ def test_tree_outputs_follow_root_to_node_paths(kind):
     assert not tree.err
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_tree_commit_compacts_the_accepted_path(kind):
     """After commit_tree the committed window holds exactly the accepted path's records in
     consecutive slots, and S is the state after that path: the same as verifying the path
@@ -103,7 +103,7 @@ def test_tree_commit_compacts_the_accepted_path(kind):
             C = wl.capacity
             for j in range(k):
                 slot = int((nc0[i] + j) % C)
-                for f in ("alpha", "v", "k", "q") + (("beta",) if kind == "gdn" else ()):
+                for f in ("alpha", "v", "k", "q") + (("beta",) if kind != "mamba2" else ()):
                     src = d[f][i, int(path[i, j])]
                     assert np.array_equal(tree.ring[f][i, slot], src)
             assert tree.n_committed[i] == nc0[i] + k
