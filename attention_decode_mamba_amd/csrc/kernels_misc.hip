@@ -70,10 +70,16 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
   __syncthreads();
   if (t == 0) {
     int ok = acc >= 0 && acc <= T && hb + T <= C;
+    // the parent rows the verify accepted: each -1 or an earlier draft (otherwise the
+    // verify appended nothing for this sequence)
+    for (int d = 0; ok && d < T; ++d)
+      if (s_par[d] < -1 || s_par[d] >= d) ok = 0;
+    // a chain from the head; with valid parents every entry is a later draft than the
+    // previous one, so path[i] >= i and the moves below read each source first
     int prev = -1;
     for (int j = 0; ok && j < acc; ++j) {
       const int d = s_path[j];
-      if (d < 0 || d >= T || s_par[d] != prev)
+      if (d < 0 || d >= T || d <= prev || s_par[d] != prev)
         ok = 0;
       else
         prev = d;

@@ -414,6 +414,7 @@ const char *rssm_strerror(int code) {
     if (code & RSSM_DEVERR_CURSOR) return "device: inconsistent cursor counters";
     if (code & RSSM_DEVERR_VERIFY_CAPACITY) return "device: verify would overflow the ring (h + T > capacity)";
     if (code & RSSM_DEVERR_ACCEPT_RANGE) return "device: accepted count out of range";
+    if (code & RSSM_DEVERR_TREE) return "device: draft tree with a parent that is not -1 or an earlier draft";
   }
   return "unknown error";
 }

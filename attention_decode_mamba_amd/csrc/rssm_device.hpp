@@ -140,21 +140,26 @@ __device__ __forceinline__ void frag_load(Frag<N, RGW> &F, const float *__restri
   }
 }
 
+// Tiles written back are stored with nontemporal, device-scope (sc1) buffer stores: the
+// lines go through the XCD's L2 without displacing what the running workgroups still read
+// (a layer's checkpoint is next read a whole step of the other layers later).  The tile
+// base is uniform across the workgroup, so it fits a buffer descriptor.
 template <int N, int RGW>
 __device__ __forceinline__ void frag_store(const Frag<N, RGW> &F, float *__restrict__ tile, int P, int wave,
                                            int lane) {
+  constexpr int kNtSc1 = 2 | 16;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tile, 0, P * N * 4, 0x00020000);
   const int c = frag_col(lane);
 #pragma unroll
   for (int i = 0; i < RGW; ++i) {
     const int row = frag_row(wave, lane, i);
     if (row < P) {
-      float4 *dst = (float4 *)(tile + (int64_t)row * N + c);
 #pragma unroll
       for (int f = 0; f < N / 32; ++f) {
         const float4 x = F.s[i][f];
         f4v v;
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        __builtin_nontemporal_store(v, (f4v *)(dst + 8 * f));
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (row * N + c + 32 * f) * 4, 0, kNtSc1);
       }
     }
   }

@@ -257,67 +257,116 @@ def _stream_copy_gbps(R, torch, stream, sh):
 
 
 # ----------------------------------------------------------------------------- decode
+def window_phases(wl, n_per_layer: int, staggered: bool):
+    """Records each sequence's window holds after the append, at a layer's n-th launch:
+    sequence b starts with b mod L records when staggered, with none in lockstep."""
+    import numpy as np
+    start = np.arange(wl.batch) % wl.L if staggered else np.zeros(wl.batch, np.int64)
+    return (start + n_per_layer) % wl.L + 1
+
+
+def launch_bytes(wl, hs) -> dict:
+    """Algorithmic bytes of one decode launch whose sequences hold hs records (after the append)."""
+    import numpy as np
+    one = wl.replace(batch=1)
+    out = {"state": 0, "total": 0}
+    for h, c in zip(*np.unique(np.asarray(hs), return_counts=True)):
+        sb = step_bytes(one, int(h))
+        out["state"] += int(c) * sb["state"]
+        out["total"] += int(c) * sb["total"]
+    return out
+
+
+def stagger_windows(R, torch, wl, cfg, ds, drafts, sh):
+    """Stagger the windows through the API (untimed): L - 1 rounds of verify(T=1) + commit,
+    sequence b accepting its draft in the first b mod L rounds, so it starts with b mod L
+    records and B / L sequences fold on every later decode step."""
+    import numpy as np
+    B = wl.batch
+    o = torch.empty(B, 1, wl.n_heads, wl.dv, device="cuda")
+    keep = []
+    for r in range(wl.L - 1):
+        d = drafts[r]
+        R.rssm_verify(cfg, ds.st, 1, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
+                      o.data_ptr(), sh)
+        acc = torch.from_numpy((np.arange(B) % wl.L > r).astype(np.int32)).cuda()
+        keep.append(acc)
+        R.rssm_commit(cfg, ds.st, acc.data_ptr(), 1, sh)
+    torch.cuda.synchronize()
+
+
 def run_decode(args, wl, with_conventional=True) -> dict:
     """Replay decode over `layers` independent layer instances, used round robin (launch n
     steps layer n % layers), so no layer's state or read copy is still cached when it is read
-    again.  Timed: `reps` repetitions of K launches each, the median reported; then K more
-    launches with an event pair around each (per-launch durations for the roofline)."""
+    again.
+
+    Windows are staggered by default (sequence b starts with b mod L records), so every
+    launch carries the window-average share of folds (B / L sequences fold on every step)
+    and any K measures the window average; --lockstep starts every window together.  Timed:
+    `reps` repetitions of K launches each, the median reported; then K more launches with an
+    event pair around each (per-launch durations for the roofline).  With staggered windows
+    a lockstep pass over whole windows (K rounded up to layers x L launches) gives the fold
+    and non-fold step times as well."""
     import statistics
     import torch
     from attention_decode_mamba_amd import rssm as R
     from attention_decode_mamba_amd.state import DeviceState, config_of
 
     K, W, layers, reps = args.steps, args.warmup, max(1, args.layers), max(1, args.reps)
+    staggered = not args.lockstep
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    print(f"[bench] {wl.name}: generating inputs for {W + K} steps, {layers} layer instances",
-          file=sys.stderr, flush=True)
+    n_in = W + K if not args.distinct else min(args.distinct, W + K)
+    print(f"[bench] {wl.name}: generating inputs for {n_in} steps, {layers} layer instances, "
+          f"{'staggered' if staggered else 'lockstep'} windows", file=sys.stderr, flush=True)
     t0 = time.time()
     s0 = _s0_device(wl, torch)
-    inputs = _gen_inputs(wl, W + K, torch)
+    inputs = _gen_inputs(wl, n_in, torch)
+    drafts = _gen_inputs(wl, wl.L - 1, torch, drafts_T=1) if staggered else None
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     cfg = config_of(wl)
     states = [DeviceState(cfg) for _ in range(layers)]
-    for ds in states:
-        ds.init(s0, sh)
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
-    count = [0]                                   # launches so far
+    count = [0]                                   # launches since the states were set up
+
+    def setup(stag):
+        for ds in states:
+            ds.init(s0, sh)
+            if stag:
+                stagger_windows(R, torch, wl, cfg, ds, drafts, sh)
+        count[0] = 0
 
     def replay(t):
-        d = inputs[t]
+        d = inputs[t % n_in]
         ds = states[count[0] % layers]
         count[0] += 1
         R.rssm_decode_step(cfg, ds.st, _p(d["alpha"]), _p(d["beta"]), _p(d["v"]), _p(d["k"]), _p(d["q"]),
                            y.data_ptr(), sh)
 
-    def phase(n):                                 # records in launch n's window after the append
-        return ((n // layers) % wl.L) + 1
+    def bytes_of(n, stag):                        # launch n since set-up
+        return launch_bytes(wl, window_phases(wl, n // layers, stag))
 
     tm = _Timer(torch, stream)
+    setup(staggered)
     for t in range(W):
         replay(t)
     rep_ms, rep_state, rep_total = [], [], []
     for _ in range(reps):
         n0 = count[0]
         rep_ms.append(tm.total_ms(lambda i: replay(W + i), K))
-        hs = [phase(n0 + i) for i in range(K)]
-        rep_state.append(sum(step_bytes(wl, h)["state"] for h in hs))
-        rep_total.append(sum(step_bytes(wl, h)["total"] for h in hs))
+        bs = [bytes_of(n0 + i, staggered) for i in range(K)]
+        rep_state.append(sum(b_["state"] for b_ in bs))
+        rep_total.append(sum(b_["total"] for b_ in bs))
     med = sorted(range(reps), key=lambda r: rep_ms[r])[reps // 2]
     total_ms, alg_state, alg_total = rep_ms[med], rep_state[med], rep_total[med]
     n0 = count[0]
     (per,) = tm.per_launch_ms([lambda i: replay(W + i)], K)
     for ds in states:
         assert ds.error() == 0
-
-    hs = [phase(n0 + i) for i in range(K)]
-    alg_launch = sum(step_bytes(wl, h)["total"] for h in hs) / K
+    alg_launch = sum(bytes_of(n0 + i, staggered)["total"] for i in range(K)) / K
     kern_ms = sum(per)
-    fold = [p for p, h in zip(per, hs) if h == wl.L]
-    nonfold = [p for p, h in zip(per, hs) if h != wl.L]
-    nf_bytes = [step_bytes(wl, h)["total"] for h in hs if h != wl.L]
     achieved = alg_launch / (kern_ms / K * 1e-3) / 1e9
     B = wl.batch
     res = {
@@ -331,19 +380,46 @@ def run_decode(args, wl, with_conventional=True) -> dict:
         "total_GBps": alg_total / (total_ms * 1e-3) / 1e9,
         "state_pct_of_peak": 100.0 * alg_state / (total_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "kernel_ms_per_launch": kern_ms / K,
-        "fold_step_ms": sum(fold) / max(len(fold), 1),
-        "nonfold_step_ms": sum(nonfold) / max(len(nonfold), 1),
-        "nonfold_GBps": (sum(nf_bytes) / len(nf_bytes)) / (sum(nonfold) / len(nonfold) * 1e-3) / 1e9
-        if nonfold else None,
+        "windows": (f"staggered: sequence b starts with b mod {wl.L} records, so {B // wl.L} of {B} "
+                    f"sequences fold on every step" if staggered else "lockstep: every sequence folds on "
+                    f"the same step, once per {wl.L} steps"),
         "timing": {"layers": layers, "reps": reps, "rep_ms_per_step": [m / K for m in rep_ms],
-                   "median_rep": med, "spread": (max(rep_ms) - min(rep_ms)) / statistics.median(rep_ms)},
+                   "median_rep": med, "spread": (max(rep_ms) - min(rep_ms)) / statistics.median(rep_ms),
+                   "launch_ms_min": min(per), "launch_ms_max": max(per),
+                   "distinct_input_steps": n_in},
     }
+
+    # lockstep over whole windows: every repetition covers the same window phases
+    period = layers * wl.L
+    Kw = period * max(1, -(-K // period)) if staggered else (K if K % period == 0 else None)
+    if Kw:
+        if staggered:
+            setup(False)
+            for t in range(period):
+                replay(t)
+        lms = [tm.total_ms(lambda i: replay(i), Kw) for _ in range(reps)]
+        n0 = count[0]
+        (lper,) = tm.per_launch_ms([lambda i: replay(i)], Kw)
+        for ds in states:
+            assert ds.error() == 0
+        hs = [int(window_phases(wl, (n0 + i) // layers, False)[0]) for i in range(Kw)]
+        fold = [p for p, h in zip(lper, hs) if h == wl.L]
+        nonfold = [p for p, h in zip(lper, hs) if h != wl.L]
+        lb = [bytes_of(n0 + i, False) for i in range(Kw)]
+        lms_med = statistics.median(lms)
+        res["lockstep"] = {
+            "ms_per_step": lms_med / Kw, "tokens_per_s": B * Kw / (lms_med * 1e-3), "launches": Kw,
+            "fold_step_ms": sum(fold) / max(len(fold), 1),
+            "nonfold_step_ms": sum(nonfold) / max(len(nonfold), 1),
+            "state_pct_of_peak": 100.0 * sum(b_["state"] for b_ in lb) / (lms_med * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "frac": sum(b_["total"] for b_ in lb) / (sum(lper) * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "spread": (max(lms) - min(lms)) / lms_med}
     if with_conventional:
         convs = [s0.clone() for _ in range(layers)]
         ccount = [0]
 
         def conventional(t):
-            d = inputs[t]
+            d = inputs[t % n_in]
             conv = convs[ccount[0] % layers]
             ccount[0] += 1
             R.rssm_decode_step_conventional(cfg, conv.data_ptr(), _p(d["alpha"]), _p(d["beta"]), _p(d["v"]),
@@ -495,7 +571,7 @@ def run_verify(args, wl, tree=False, fused=False) -> dict:
     if fused:                               # the fused call keeps h + T <= C before its fold
         wl = wl.replace(capacity=wl.L + 2 * T - 1)
     K, W = args.steps, args.warmup
-    distinct = min(args.distinct, W + K)
+    distinct = min(args.distinct or 16, W + K)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -630,7 +706,7 @@ def run_verify_snapshot(args, wl) -> dict:
 
     T = wl.t_max
     K, W = args.steps, args.warmup
-    distinct = min(args.distinct, W + K)
+    distinct = min(args.distinct or 16, W + K)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -752,7 +828,10 @@ def _read_counter_csv(path):
 def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, warmup, layers, reps):
     """Per-launch HBM traffic of the decode and conventional kernels from two --pmc runs
     (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
-    reads for the streaming copy of COPY_BYTES bytes."""
+    reads for the streaming copy of COPY_BYTES bytes.  The decode figure averages the
+    launches of the headline's staggered windows (the first warmup + (reps + 1) * steps
+    decode dispatches of the bench run; the lockstep pass follows them), whose
+    algorithmic bytes are the same for every launch."""
     from synth import get_workload
     wl = get_workload(WORKLOAD).replace(batch=batch)
     res = {"kernel_source_hash": kernel_source_hash(), "batch": batch, "command": command,
@@ -760,8 +839,9 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, wa
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
 
-    def per_kernel(table, counter, key):
-        return [c.get(counter, 0.0) for n, c in table.values() if key in n]
+    def per_kernel(table, counter, key):               # in dispatch order
+        rows = sorted(((int(d), n, c) for d, (n, c) in table.items() if d is not None), key=lambda r: r[0])
+        return [c.get(counter, 0.0) for _, n, c in rows if key in n]
 
     cf = per_kernel(fetch, "FETCH_SIZE", "k_stream_copy")
     cw = per_kernel(write, "WRITE_SIZE", "k_stream_copy")
@@ -771,9 +851,10 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, wa
     res["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_mean": sum(cf) / len(cf),
                                "write_kib_mean": sum(cw) / len(cw), "fetch_scale": ff, "write_scale": fw,
                                "dispatches": len(cf)}
-    for key, label in (("k_decode", "replay_decode"), ("k_conventional", "conventional")):
-        f = per_kernel(fetch, "FETCH_SIZE", key)
-        w = per_kernel(write, "WRITE_SIZE", key)
+    n_stag = warmup + (reps + 1) * steps
+    for key, label, first in (("k_decode", "replay_decode", n_stag), ("k_conventional", "conventional", None)):
+        f = per_kernel(fetch, "FETCH_SIZE", key)[:first]
+        w = per_kernel(write, "WRITE_SIZE", key)[:first]
         if not f or not w:
             continue
         fb = sum(f) / len(f) * 1024.0 * ff
@@ -781,16 +862,13 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, wa
         res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                       "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
                       "write_mib_per_dispatch_min_max": [min(w) / 1024.0 * fw, max(w) / 1024.0 * fw]}
-    # every decode dispatch of the run: warmup, the timed repetitions and the per-launch pass;
-    # dispatch n steps layer n % layers
-    n = warmup + (reps + 1) * steps
-    hs = [((i // layers) % wl.L) + 1 for i in range(n)]
-    alg = sum(step_bytes(wl, h)["total"] for h in hs) / n
-    res["algorithmic_bytes_per_launch"] = alg
+    alg = launch_bytes(wl, window_phases(wl, 0, True))
+    res["algorithmic_bytes_per_launch"] = alg["total"]
+    res["algorithmic_state_bytes_per_launch"] = alg["state"]
     if "replay_decode" in res:
         r = res["replay_decode"]
         res["traffic_bytes_per_launch"] = r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
-        res["traffic_over_algorithmic"] = res["traffic_bytes_per_launch"] / alg
+        res["traffic_over_algorithmic"] = res["traffic_bytes_per_launch"] / alg["total"]
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
     return res
@@ -804,11 +882,14 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch of the headline workload")
     ap.add_argument("--layers", type=int, default=4, help="layer instances used round robin (decode workloads)")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions of K steps; the median is reported")
+    ap.add_argument("--lockstep", action="store_true",
+                    help="decode workloads: start every window together instead of staggered")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=[WORKLOAD, "gdn_b256", "kda_b256", "m2_readcopy_b256", "m2_verify_b512",
                              "gdn_verify_b256", "kda_verify_b256"])
     ap.add_argument("--read-copy", default="fp8", choices=["fp8", "mxfp4"])
-    ap.add_argument("--distinct", type=int, default=16, help="distinct draft batches (verify workloads)")
+    ap.add_argument("--distinct", type=int, default=0,
+                    help="distinct input batches, cycled (0: every step distinct for decode, 16 for verify)")
     ap.add_argument("--tree", action="store_true", help="verify workloads: tree-shaped drafts (verify_tree/commit_tree)")
     ap.add_argument("--fused", action="store_true", help="verify workloads: flush fused into the next verify")
     ap.add_argument("--snapshot", action="store_true",

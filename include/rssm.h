@@ -161,9 +161,12 @@ int rssm_sizes(const rssm_config *cfg, rssm_buffer_sizes *out);
  * beta's offset equals v's when kind is Mamba-2). */
 int rssm_ring_offsets(const rssm_config *cfg, int64_t *out5);
 
-/* Initialise a state: S_ckpt <- s0 (fp32 [B][H][dv][dk]) or zeros when s0 == NULL,
- * write the read copy, zero the counters and the error word.  The ring content is
- * left as is (no live records). */
+/* Initialise a state (page 4 "What shipped": the state is kept as a checkpoint plus a
+ * buffer of recent records; page 1, low-precision paragraph of the section on what got
+ * faster: the low-precision copy is made from the checkpoint): S_ckpt <- s0 (fp32
+ * [B][H][dv][dk]) or zeros when s0 == NULL, write the read copy from it, set both
+ * counters to 0 (an empty window) and clear the error word.  The ring content is left
+ * as is (no live records). */
 int rssm_init_state(const rssm_config *cfg, const rssm_state *st, const float *s0,
                     hipStream_t stream);
 
@@ -212,7 +215,9 @@ int rssm_verify(const rssm_config *cfg, const rssm_state *st, int32_t T, const v
  * move): n_committed += n_accept[b] for every sequence, nothing else.  n_accept is
  * int32 [B] on the device, each in 0..T where T is the preceding verify's T.  An
  * out-of-range value (or a sequence whose verify could not append) sets
- * RSSM_DEVERR_ACCEPT_RANGE and leaves that sequence untouched. */
+ * RSSM_DEVERR_ACCEPT_RANGE and leaves that sequence untouched.  It commits a linear
+ * rssm_verify; a tree verify is committed with rssm_commit_tree, which also refuses the
+ * sequences whose tree the verify refused (rssm_commit cannot tell them). */
 int rssm_commit(const rssm_config *cfg, const rssm_state *st, const int32_t *n_accept,
                 int32_t T, hipStream_t stream);
 
@@ -250,13 +255,16 @@ int rssm_verify_fold(const rssm_config *cfg, const rssm_state *st, int32_t min_r
  * each next entry is a child of the previous one; parent as passed to the verify).  The
  * accepted drafts' ring records move to slots (n_committed + i) % C, i < n_accept[b], so
  * the committed window stays contiguous; then n_committed += n_accept[b].  A path that
- * is not such a chain, n_accept outside 0..T, or h + T > C sets RSSM_DEVERR_ACCEPT_RANGE
- * and leaves the sequence untouched.  Follow with rssm_flush(L) as after rssm_commit. */
+ * is not such a chain, n_accept outside 0..T, h + T > C, or a parent row the verify
+ * refused (an entry not -1 or an earlier draft: its drafts were never appended) sets
+ * RSSM_DEVERR_ACCEPT_RANGE and leaves the sequence untouched.  Follow with
+ * rssm_flush(L) as after rssm_commit. */
 int rssm_commit_tree(const rssm_config *cfg, const rssm_state *st, const int32_t *parent,
                      const int32_t *path, const int32_t *n_accept, int32_t T, hipStream_t stream);
 
 /* Conventional read-modify-write decode step, the comparison point (page 4 "What
- * shipped": every token loads the full state, updates it and stores it back).
+ * shipped": the standard kernel reads the whole state, applies the rank-1 update and
+ * writes the state out again on every token).
  * s: fp32 [B][H][dv][dk] state, updated in place; inputs and y as in
  * rssm_decode_step.  No ring, no cursor. */
 int rssm_decode_step_conventional(const rssm_config *cfg, float *s, const void *alpha,

@@ -1,9 +1,9 @@
 """Checkpoint + ring + cursor model of ReplaySSM, stepwise in float64 (oracle).
 
 TEST INFRASTRUCTURE ONLY.  Pages: page 4 "What shipped" (window of L buffered
-records, flush on a full buffer, drafts appended and the accepted prefix
-committed by advancing a pointer, records past the pointer ignored and
-overwritten); page 1, section on what the method does (flush writes the state
+records, flush on a full buffer, drafts added to the buffer and acceptance
+recorded by moving the cursor forward, records beyond the cursor dead until
+written over); page 1, section on what the method does (flush writes the state
 once and empties the buffer) and section on what got faster (speculative
 drafts appended to the buffer; the pointer advances by the accepted count; a
 low-precision copy serves reads and never re-enters the recurrence).
@@ -151,10 +151,15 @@ class ReplayOracle:
 
     # -- operations ------------------------------------------------------------
     def decode(self, inp) -> np.ndarray:
-        """One decode step; ``inp`` arrays have leading dim len(seqs).  Returns y [nb,H,P]."""
+        """One decode step; ``inp`` arrays have leading dim len(seqs).  Returns y [nb,H,P].
+
+        With a read copy, non-flush outputs come from the copy's chain; ``self.y_exact``
+        then holds the outputs of the full-precision recurrence for the same step (without
+        one, both are the same)."""
         wl = self.wl
         nb = len(self.seqs)
         y = np.full((nb, wl.n_heads, wl.dv), np.nan)
+        self.y_exact = np.full((nb, wl.n_heads, wl.dv), np.nan)
         for i in range(nb):
             slot = int(self.n_committed[i] % wl.capacity)
             self._store(i, slot, inp)
@@ -163,6 +168,7 @@ class ReplayOracle:
             if self.track_state:
                 rec = self._rec(inp, i)
                 self.S[i], y_full = step(wl.kind, self.S[i], rec)
+                self.y_exact[i] = y_full
                 if self.R is not None and not flush:
                     self.R[i], y[i] = step(wl.kind, self.R[i], rec)
                     if self.read_tol is not None:

@@ -13,6 +13,7 @@ from .gen import (
     decode_inputs,
     draft_inputs,
     accept_counts, draft_tree,
+    special_decode_inputs, special_draft_inputs,
     stack_decode_inputs,
     stack_draft_inputs,
 )
@@ -21,5 +22,6 @@ __all__ = [
     "WORKLOADS", "Workload", "get_workload",
     "bf16_bits_from_f32", "head_params", "initial_state",
     "decode_inputs", "draft_inputs", "accept_counts", "draft_tree",
+    "special_decode_inputs", "special_draft_inputs",
     "stack_decode_inputs", "stack_draft_inputs",
 ]

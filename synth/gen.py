@@ -17,6 +17,11 @@ Distributions (per the workload descriptions):
   channel) instead of per head.
 * Initial state S0 ~ N(0, 0.1) (variance) in float32, or zero.
 * Accepted draft count per (sequence, verify step) ~ U{0, ..., T}.
+* Special records (``special_decode_inputs`` / ``special_draft_inputs``): the records
+  above with exact special values mixed in by head and record index r: alpha 0 or 1
+  (KDA: all channels 0, all 1, or alternating 0/1), beta 0 or 1, a unit basis vector as
+  the key, one fixed key repeated in every record of a (sequence, key head), and q equal
+  to k.
 """
 from __future__ import annotations
 
@@ -35,6 +40,8 @@ _TAG_DECODE = 0x01
 _TAG_DRAFT = 0x02
 _TAG_ACCEPT = 0x03
 _TAG_TREE = 0x04
+_TAG_SPECIAL = 0x05
+_TAG_SPECIAL_KEY = 0x06
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -98,6 +105,72 @@ def _record(wl: Workload, g: np.random.Generator, hp: Dict[str, np.ndarray]):
     else:
         raise ValueError(wl.kind)
     return alpha, beta, v, k, q
+
+
+def _fixed_key(wl: Workload, b: int, g: int) -> np.ndarray:
+    """A key that repeats in every special record of (sequence b, key head g)."""
+    k = _rng(wl.seed, _TAG_SPECIAL_KEY, b, g).standard_normal(wl.dk)
+    return k / (np.sqrt(wl.dk) if wl.kind == "mamba2" else np.linalg.norm(k))
+
+
+def _special_record(wl: Workload, g: np.random.Generator, hp, b: int, r: int):
+    """Record r of sequence b with special values mixed in (float64, before the cast)."""
+    alpha, beta, v, k, q = _record(wl, g, hp)
+    H, G, N = wl.n_heads, wl.n_qk_heads, wl.dk
+    for h in range(H):
+        m = (h + r) % 4
+        if wl.kind == "kda":
+            if m == 0:
+                alpha[h] = 0.0
+            elif m == 1:
+                alpha[h] = 1.0
+            elif m == 2:
+                alpha[h] = np.arange(N) % 2
+        elif m < 2:
+            alpha[h] = float(m)
+        if beta is not None and (h + 2 * r) % 3 < 2:
+            beta[h] = float((h + 2 * r) % 3)
+    for gg in range(G):
+        m = (gg + r) % 3
+        if m == 0:
+            k[gg] = 0.0
+            k[gg, (r + gg) % N] = 1.0
+        elif m == 1:
+            k[gg] = _fixed_key(wl, b, gg)
+        if (gg + r) % 2 == 0:
+            q[gg] = k[gg]
+    return alpha, beta, v, k, q
+
+
+def special_decode_inputs(wl: Workload, step: int, seqs: Sequence[int]):
+    """Decode inputs of one step with special values mixed in (record index r = step)."""
+    hp = head_params(wl)
+    out = _empty(wl, (len(seqs),))
+    for i, b in enumerate(seqs):
+        a, be, v, k, q = _special_record(wl, _rng(wl.seed, _TAG_SPECIAL, step, b), hp, b, step)
+        _put(out, (i,), wl, a, be, v, k, q)
+    return out
+
+
+def special_draft_inputs(wl: Workload, step: int, seqs: Sequence[int], T: int):
+    """T draft records of one verify step with special values (record index r = step * T + tau)."""
+    hp = head_params(wl)
+    out = _empty(wl, (len(seqs), T))
+    for i, b in enumerate(seqs):
+        g = _rng(wl.seed, _TAG_SPECIAL, 1 << 20, step, b)
+        for t in range(T):
+            a, be, v, k, q = _special_record(wl, g, hp, b, step * T + t)
+            _put(out, (i, t), wl, a, be, v, k, q)
+    return out
+
+
+def _put(out, idx, wl, a, be, v, k, q):
+    out["alpha"][idx] = _cast(a, wl.in_dtype)
+    if be is not None:
+        out["beta"][idx] = _cast(be, wl.in_dtype)
+    out["v"][idx] = _cast(v, wl.in_dtype)
+    out["k"][idx] = _cast(k, wl.in_dtype)
+    out["q"][idx] = _cast(q, wl.in_dtype)
 
 
 def _empty(wl: Workload, lead: tuple) -> Dict[str, Optional[np.ndarray]]:

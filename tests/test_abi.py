@@ -30,6 +30,17 @@ def test_version_and_strerror():
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert isinstance(R.rssm_strerror(code), str) and R.rssm_strerror(code)
     assert "ring" in R.rssm_strerror(R.RSSM_DEVERR_VERIFY_CAPACITY)
+    # every device error bit has its own message, alone and as the only bit of a word
+    bits = {R.RSSM_DEVERR_VERIFY_CAPACITY: "ring", R.RSSM_DEVERR_ACCEPT_RANGE: "accepted",
+            R.RSSM_DEVERR_CURSOR: "cursor", R.RSSM_DEVERR_TREE: "tree"}
+    msgs = set()
+    for bit, word in bits.items():
+        m = R.rssm_strerror(bit)
+        assert m.startswith("device:") and word in m, (bit, m)
+        msgs.add(m)
+    assert len(msgs) == len(bits)
+    assert R.rssm_strerror(16) == "unknown error"              # no such bit
+    assert R.rssm_strerror(R.RSSM_DEVERR_TREE | 16).startswith("device:")
 
 
 def test_sizes_serving_shape():

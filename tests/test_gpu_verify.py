@@ -416,6 +416,43 @@ def test_tree_contract_errors():
     assert nc[:, 0].tolist() == [2, 0, 0, 0, 0, 0]
 
 
+def test_tree_commit_refuses_a_tree_the_verify_refused():
+    """A parent row the verify refused (draft 0 hanging off the later draft 1) appended
+    nothing, so a commit of it must move nothing either, even for a path that follows that
+    row's parent links ([1, 0]): RSSM_DEVERR_ACCEPT_RANGE, cursor and ring unchanged.  The
+    oracle refuses the same commit."""
+    wl = _small("m2_verify_b512")
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    orc = ReplayOracle(wl, seqs, S0)
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    dr = draft_inputs(wl, 0, seqs, T)
+    d = to_dev_inputs(dr)
+    parent = np.tile(np.array([-1, 0, 0, 1], np.int32), (wl.batch, 1))
+    parent[2] = [1, -1, 0, 1]
+    par_d = dev(parent)
+    R.rssm_verify_tree(ds.cfg, ds.st, T, ptr(par_d), ptr(d["alpha"]), None, ptr(d["v"]), ptr(d["k"]), ptr(d["q"]),
+                       ptr(o), stream())
+    orc.verify_tree(dr, T, parent)
+    assert ds.error() == R.RSSM_DEVERR_TREE
+    ring_before = {k: (None if v is None else v.clone()) for k, v in ds.ring_arrays().items()}
+    path = np.full((wl.batch, T), -1, np.int32)
+    path[:, :2] = [0, 1]
+    path[2, :2] = [1, 0]
+    acc = np.full(wl.batch, 2, np.int32)
+    path_d, acc_d = dev(path), dev(acc)           # alive until the kernel has run
+    R.rssm_commit_tree(ds.cfg, ds.st, ptr(par_d), ptr(path_d), ptr(acc_d), T, stream())
+    orc.commit_tree(path, acc, T)
+    assert ds.error() == R.RSSM_DEVERR_ACCEPT_RANGE and orc.err
+    nc, _ = counters(ds)
+    assert nc[:, 0].tolist() == [2, 2, 0, 2, 2, 2] == orc.n_committed.tolist()
+    ring_after = ds.ring_arrays()
+    for k in ("alpha", "v", "k", "q"):
+        assert torch.equal(ring_before[k][2], ring_after[k][2]), k
+
+
 def test_invalid_tree_in_fused_verify_leaves_sequence_untouched():
     """verify_fold with an invalid draft tree: that sequence is neither folded nor appended
     (checkpoint bits, n_ckpt and ring unchanged), RSSM_DEVERR_TREE is set; the other

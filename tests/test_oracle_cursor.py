@@ -1,9 +1,9 @@
 """Pins of the oracle's integer cursor policy and the rollback invariant.
 
-Page 4 "What shipped": a 16-record window with a flush when it fills; drafts are
-appended and the accepted prefix is committed by advancing a pointer; records
-past the pointer are ignored and overwritten.  Page 1 (what got faster): no
-snapshots and no state to roll back.
+Page 4 "What shipped": the window holds 16 records and is folded when full;
+speculative drafts go into the buffer, acceptance moves the cursor forward, and
+any record beyond the cursor is dead and will simply be written over later.
+Page 1 (what got faster): rollback needs neither snapshots nor a state restore.
 """
 import json
 import os
