@@ -36,11 +36,13 @@ def _decode_seq(args):
 
 
 def _spec_seq(args):
-    wl, b, decode_steps, verify_steps, T, keep_ckpt = args
+    wl, b, decode_steps, verify_steps, T, keep_ckpt, keep_dec = args
     orc = ReplayOracle(wl, [b], initial_state(wl, [b]))
-    yd = []
+    yd, ckd = [], {}
     for t in range(decode_steps):
         yd.append(orc.decode(decode_inputs(wl, t, [b]))[0])
+        if keep_dec(t):
+            ckd[t] = orc.S_ckpt[0].copy()
     O, nc, nk, ck = [], [], [], {}
     for s in range(verify_steps):
         O.append(orc.verify(draft_inputs(wl, s, [b], T), T)[0])
@@ -51,7 +53,7 @@ def _spec_seq(args):
         if keep_ckpt(s):
             ck[s] = orc.S_ckpt[0].copy()
     return dict(y=np.array(yd) if yd else None, O=np.array(O), nc=np.array(nc), nk=np.array(nk),
-                ckpt=ck, err=orc.err)
+                ckpt=ck, ckpt_decode=ckd, err=orc.err)
 
 
 class _Every:
@@ -71,8 +73,12 @@ def decode_runs(wl, seqs: Sequence[int], steps: int, ckpt_every: int = 0) -> Dic
 
 def spec_runs(wl, seqs: Sequence[int], decode_steps: int, verify_steps: int, T: int,
               ckpt_every: int = 0) -> Dict[int, dict]:
+    """Decode then verify -> commit -> flush(L) per sequence.  Checkpoints are kept every
+    ckpt_every steps of each phase (and after its last step): ``ckpt`` (verify phase) and
+    ``ckpt_decode`` (decode phase)."""
     keep = _Every(ckpt_every, verify_steps - 1)
-    jobs = [(wl, b, decode_steps, verify_steps, T, keep) for b in seqs]
+    keep_dec = _Every(ckpt_every, decode_steps - 1)
+    jobs = [(wl, b, decode_steps, verify_steps, T, keep, keep_dec) for b in seqs]
     with ProcessPoolExecutor(max_workers=max(1, min(default_workers(), len(jobs)))) as ex:
         return dict(zip(seqs, ex.map(_spec_seq, jobs)))
 

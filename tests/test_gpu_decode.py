@@ -85,6 +85,11 @@ SHAPES = [
     ("kda", "fp32", 2, 2, 2, 128, 128, 16, 16),
     ("kda", "bf16", 2, 2, 2, 33, 32, 3, 3),         # rows not 16-byte aligned: element-wise staging
     ("kda", "bf16", 2, 2, 1, 128, 128, 32, 32),
+    # the widest tiles: 16 row groups of 8 per wave at dk = 32, 8 at dk = 64
+    ("mamba2", "bf16", 2, 2, 2, 512, 32, 5, 5),
+    ("gdn", "fp32", 2, 2, 1, 512, 32, 4, 4),
+    ("kda", "bf16", 2, 2, 2, 500, 32, 4, 4),
+    ("mamba2", "fp32", 2, 2, 2, 256, 64, 4, 4),
 ]
 
 _BASE = {"mamba2": "m2_tiny", "gdn": "gdn_b256", "kda": "kda_b256"}

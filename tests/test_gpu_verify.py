@@ -165,31 +165,34 @@ def test_device_errors_leave_sequences_untouched():
     assert np.all(nk4[0] == 4 * T)
 
 
-SAMPLE4 = [0, 171, 342, 511]
+SAMPLE8_512 = [0, 73, 146, 219, 292, 365, 438, 511]
+SAMPLE8_256 = [0, 37, 74, 111, 148, 185, 222, 255]
 
 
 def test_serving_shape_verify_sampled():
-    """Mamba-2 verify at B=512, H=128, P=64, N=128, T=4, 128 steps; accepted prefix ~ U{0..4}."""
+    """Mamba-2 verify at B=512, H=128, P=64, N=128, T=4, 128 steps; accepted prefix ~ U{0..4}.
+    8 sampled sequences x all heads against the oracle at every step; every cursor of the batch
+    at every step; sampled checkpoints every 32 steps."""
     wl = get_workload("m2_verify_b512")
     T, steps = wl.t_max, wl.verify_steps
     seqs = list(range(wl.batch))
-    print(f"[serving verify] oracle runs for {SAMPLE4}", flush=True)
-    ref = spec_runs(wl, SAMPLE4, 0, steps, T, ckpt_every=32)
+    print(f"[serving verify] oracle runs for {SAMPLE8_512}", flush=True)
+    ref = spec_runs(wl, SAMPLE8_512, 0, steps, T, ckpt_every=32)
     cur = cursor_run(wl, steps, verify=True, T=T)
     ds = new_state(wl, initial_state(wl, seqs))
     o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
-    idx = torch.tensor(SAMPLE4, device="cuda")
+    idx = torch.tensor(SAMPLE8_512, device="cuda")
     worst = 0.0
     with StepSource(wl, seqs) as src:
         for s in range(steps):
             verify(ds, T, to_dev_inputs(src.drafts(s, T)), o)
             got = o[idx].cpu().numpy()
-            for i, b in enumerate(SAMPLE4):
+            for i, b in enumerate(SAMPLE8_512):
                 worst = max(worst, relerr(got[i], ref[b]["O"][s]).max())
             _commit(ds, dev(accept_counts(wl, s, T)), T)
             _flush(ds, wl.L)
             assert_counters(ds, *cur[s], f"step {s}")
-            for b in SAMPLE4:
+            for b in SAMPLE8_512:
                 if s in ref[b]["ckpt"]:
                     e = tile_relerr(ds.ckpt()[b].cpu().numpy(), ref[b]["ckpt"][s]).max()
                     assert e <= TOL, f"step {s} seq {b}: checkpoint rel err {e:.3g}"
@@ -202,14 +205,17 @@ def test_serving_shape_verify_sampled():
 @pytest.mark.parametrize("name", ["gdn_b256", "kda_b256"])
 def test_serving_shape_gdn_decode_then_verify_sampled(name):
     """Gated DeltaNet at B=256, 32 value / 16 key heads, 128 x 128 tiles (KDA: 32 heads with
-    per-channel gates): 256 decode steps, then 256 verify steps with T = 4 drafts."""
+    per-channel gates): 256 decode steps, then 256 verify steps with T = 4 drafts.  8 sampled
+    sequences x all heads against the oracle at every step of both phases; every cursor of the
+    batch at every step of both phases; sampled checkpoints every 64 steps of both phases."""
     wl = get_workload(name)
     T = wl.t_max
     nd, nv = wl.decode_steps, wl.verify_steps
     seqs = list(range(wl.batch))
-    sample = [0, 128, 255]
+    sample = SAMPLE8_256
     print(f"[serving {name}] oracle runs for {sample}", flush=True)
     ref = spec_runs(wl, sample, nd, nv, T, ckpt_every=64)
+    cur_d = cursor_run(wl, nd, verify=False)
     cur = cursor_run(wl, nv, verify=True, T=T, decode_steps=nd)
     ds = new_state(wl, initial_state(wl, seqs))
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
@@ -222,6 +228,11 @@ def test_serving_shape_gdn_decode_then_verify_sampled(name):
             got = y[idx].cpu().numpy()
             for i, b in enumerate(sample):
                 worst_d = max(worst_d, relerr(got[i], ref[b]["y"][t]).max())
+            assert_counters(ds, *cur_d[t], f"decode step {t}")
+            for b in sample:
+                if t in ref[b]["ckpt_decode"]:
+                    e = tile_relerr(ds.ckpt()[b].cpu().numpy(), ref[b]["ckpt_decode"][t]).max()
+                    assert e <= TOL, f"decode step {t} seq {b}: checkpoint rel err {e:.3g}"
         print(f"[serving {name}] decode worst rel err {worst_d:.3g}", flush=True)
         for s in range(nv):
             verify(ds, T, to_dev_inputs(src.drafts(s, T)), o)
@@ -616,7 +627,26 @@ def test_spec_at_maximum_drafts_and_capacity(shape):
     LDS budget admits: linear verify -> commit -> flush(L), then tree verify -> commit_tree ->
     flush(L), then the flush fused into the verify, each against the oracle."""
     name, P, N = shape
-    wl = _small(name, batch=3, dv=P, dk=N, t_max=8, capacity=32, L=25)
+    _spec_linear_tree_fused(_small(name, batch=3, dv=P, dk=N, t_max=8, capacity=32, L=25))
+
+
+WIDE_SHAPES = [
+    # name, dv, dk: the widest tiles the kernels accept (16 row groups of 8 per wave at dk = 32,
+    # 8 at dk = 64), ragged row counts included; T = 4, C = 19, L = 16
+    ("m2_verify_b512", 512, 32),
+    ("gdn_b256", 512, 32),
+    ("kda_b256", 500, 32),
+    ("m2_verify_b512", 250, 64),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}-{s[1]}x{s[2]}")
+def test_spec_at_widest_tiles(shape):
+    name, P, N = shape
+    _spec_linear_tree_fused(_small(name, batch=3, dv=P, dk=N, t_max=4, capacity=19, L=16))
+
+
+def _spec_linear_tree_fused(wl):
     T = wl.t_max
     seqs = list(range(wl.batch))
     S0 = initial_state(wl, seqs)
@@ -639,4 +669,4 @@ def test_spec_at_maximum_drafts_and_capacity(shape):
     for s in range(12):
         _tree_step(ds, orc, wl, 100 + s, T, seqs, o)
     assert ds.error() == 0
-    _fused_loop(wl.replace(capacity=32, L=32 - 2 * T + 1), 12, tree=False)
+    _fused_loop(wl.replace(L=wl.capacity - 2 * T + 1), 12, tree=False)
