@@ -1011,8 +1011,19 @@ __device__ __forceinline__ void write_rows(const float (&part)[RGW], float G, co
 // U: staging chunks per thread per round (2 covers a 17-record Mamba-2 window at 64 x 128
 // in bf16 in one round).  RCF: the read-copy format (RSSM_READ_*); with a copy the kernel
 // serves non-fold steps from it.
+// Mamba-2 read-copy instances with rows of at least 128 columns and at most 32 tile registers
+// per lane run at 8 waves per SIMD: their non-fold steps move 4-9 KB per tile and are bound
+// by the latency of the cursor -> records + copy chain, so more workgroups in flight pay
+// off, and these instances fit 8 waves without spills (the scalar registers otherwise cap
+// them at 7).  The delta-rule folds and narrower rows would spill, so they keep the default.
+template <int KIND, int RCF, int N, int RGW>
+constexpr int decode_min_waves() {
+  return (KIND == RSSM_KIND_MAMBA2 && RCF != RSSM_READ_NONE && N >= 128 && RGW * N <= 256) ? 8 : 1;
+}
+
 template <int KIND, int N, int RGW, int RCF, int STG>
-__global__ __launch_bounds__(kThreads) void k_decode(Args a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) void k_decode(Args a) {
   constexpr int U = (KIND != RSSM_KIND_MAMBA2 || RGW > 2) ? 4 : 2;
   constexpr bool RC = RCF != RSSM_READ_NONE;
   extern __shared__ float lds[];
