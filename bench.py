@@ -448,7 +448,8 @@ def headline(args) -> dict:
     if os.path.exists(PROFILE_SUMMARY):
         with open(PROFILE_SUMMARY) as f:
             prof = json.load(f)
-        if prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("batch") == wl.batch:
+        if (prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("batch") == wl.batch
+                and prof.get("workload", WORKLOAD) == WORKLOAD):
             traffic = prof.get("traffic_bytes_per_launch")
     r["roofline"]["traffic"] = traffic
     r["roofline"]["kernel"] = "k_decode<mamba2, N=128, RGW=2>"
@@ -662,7 +663,9 @@ def run_verify(args, wl, tree=False, fused=False) -> dict:
             fb[i] = {"state": 0, "total": 0}
     v_ach = sum(b["total"] for b in vb) / (sum(pv) * 1e-3) / 1e9
     f_ach = (sum(b["total"] for b in fb) / (sum(pf) * 1e-3) / 1e9) if not fused else None
+    copy_gbps = _stream_copy_gbps(R, torch, stream, sh)
     return {
+        "stream_copy_GBps": copy_gbps,
         "metric": (f"speculative {'tree ' if tree else ''}" +
                    ("verify_fold->commit" if fused else "verify->commit->flush") +
                    f", committed tokens/s ({wl.name}, T={T})"),
@@ -740,10 +743,13 @@ def run_verify_snapshot(args, wl) -> dict:
     committed = int(sum(int(accept_dev[W + i].sum().item()) for i in range(K)))
     vb = snapshot_verify_bytes(wl, T)
     v_ach = vb["total"] / (sum(pv) / K * 1e-3) / 1e9
+    copy_gbps = _stream_copy_gbps(R, torch, stream, sh)
     return {
+        "stream_copy_GBps": copy_gbps,
         "metric": f"snapshot-based speculative verify->commit, committed tokens/s ({wl.name}, T={T})",
         "value": committed / (total_ms * 1e-3), "unit": "committed tokens/s",
         "ms_per_step": total_ms / K, "steps": K, "warmup": W, "data": "synthetic",
+        "mean_accept": committed / (K * wl.batch),
         "verify": {"ms": sum(pv) / K, "GBps": v_ach, "frac": v_ach / PEAK_HBM_GBPS,
                    "bytes_per_launch": vb["total"], "state_bytes_per_launch": vb["state"]},
         "commit": {"ms": sum(pc) / K},
@@ -825,17 +831,24 @@ def _read_counter_csv(path):
     return out
 
 
-def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, warmup, layers, reps):
-    """Per-launch HBM traffic of the decode and conventional kernels from two --pmc runs
-    (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
-    reads for the streaming copy of COPY_BYTES bytes.  The decode figure averages the
-    launches of the headline's staggered windows (the first warmup + (reps + 1) * steps
-    decode dispatches of the bench run; the lockstep pass follows them), whose
-    algorithmic bytes are the same for every launch."""
-    from synth import get_workload
-    wl = get_workload(WORKLOAD).replace(batch=batch)
-    res = {"kernel_source_hash": kernel_source_hash(), "batch": batch, "command": command,
-           "steps": steps, "warmup": warmup, "layers": layers, "reps": reps}
+def summarize_counters(fetch_csv, write_csv, out_path, command, wl, bench_json, steps, warmup, layers, reps):
+    """Per-launch HBM traffic of the kernels of one bench run from two rocprofv3 --pmc runs
+    of it (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the same
+    counter reads for the streaming copy of COPY_BYTES bytes that every bench run ends with.
+
+    Which dispatches are averaged, and against which algorithmic bytes:
+    * decode workloads: the launches of the staggered windows (the first warmup + (reps + 1)
+      * steps decode dispatches; the lockstep pass follows them), whose algorithmic bytes are
+      the same for every launch; the conventional kernel: every dispatch.
+    * speculative loops: the last `steps` dispatches of verify, commit and flush (the pass
+      with per-launch events, whose mean algorithmic bytes the bench line reports).
+    * the snapshot comparator: every dispatch (the same bytes each launch).
+    Per token: decode per sequence-step; speculative per committed token."""
+    with open(bench_json) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    res = {"kernel_source_hash": kernel_source_hash(), "workload": wl.name, "batch": wl.batch,
+           "read_copy": wl.read_copy, "command": command, "steps": steps, "warmup": warmup, "layers": layers,
+           "reps": reps}
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
 
@@ -851,24 +864,41 @@ def summarize_counters(fetch_csv, write_csv, out_path, command, batch, steps, wa
     res["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_kib_mean": sum(cf) / len(cf),
                                "write_kib_mean": sum(cw) / len(cw), "fetch_scale": ff, "write_scale": fw,
                                "dispatches": len(cf)}
-    n_stag = warmup + (reps + 1) * steps
-    for key, label, first in (("k_decode", "replay_decode", n_stag), ("k_conventional", "conventional", None)):
-        f = per_kernel(fetch, "FETCH_SIZE", key)[:first]
-        w = per_kernel(write, "WRITE_SIZE", key)[:first]
+    B = wl.batch
+    if "verify" not in bench:                                          # decode
+        alg = launch_bytes(wl, window_phases(wl, 0, True))
+        picks = [("k_decode", "replay_decode", slice(0, warmup + (reps + 1) * steps), alg["total"], B),
+                 ("k_conventional", "conventional", slice(None), conventional_bytes(wl)["total"], B)]
+        res["algorithmic_state_bytes_per_launch"] = alg["state"]
+    elif bench["roofline"]["kernel"] == "k_verify_snapshot":
+        per_tok = bench["mean_accept"] * B
+        picks = [("k_verify_snapshot", "verify_snapshot", slice(None), bench["verify"]["bytes_per_launch"], per_tok),
+                 ("k_commit_snapshot", "commit_snapshot", slice(None), None, per_tok)]
+    else:
+        per_tok = bench["mean_accept"] * B
+        picks = [("k_verify", "verify", slice(-steps, None), bench["verify"]["bytes_per_launch"], per_tok),
+                 ("k_commit_tree" if "tree" in bench["metric"] else "k_commit", "commit", slice(-steps, None), None,
+                  per_tok),
+                 ("k_flush", "flush", slice(-steps, None), bench["flush"]["bytes_per_launch"], per_tok)]
+    for key, label, sl, alg_b, per in picks:
+        f = per_kernel(fetch, "FETCH_SIZE", key)[sl]
+        w = per_kernel(write, "WRITE_SIZE", key)[sl]
         if not f or not w:
             continue
         fb = sum(f) / len(f) * 1024.0 * ff
         wb = sum(w) / len(w) * 1024.0 * fw
-        res[label] = {"dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                      "fetch_bytes_per_token": fb / batch, "write_bytes_per_token": wb / batch,
-                      "write_mib_per_dispatch_min_max": [min(w) / 1024.0 * fw, max(w) / 1024.0 * fw]}
-    alg = launch_bytes(wl, window_phases(wl, 0, True))
-    res["algorithmic_bytes_per_launch"] = alg["total"]
-    res["algorithmic_state_bytes_per_launch"] = alg["state"]
-    if "replay_decode" in res:
-        r = res["replay_decode"]
-        res["traffic_bytes_per_launch"] = r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
-        res["traffic_over_algorithmic"] = res["traffic_bytes_per_launch"] / alg["total"]
+        ent = {"kernel": key, "dispatches": len(f), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+               "traffic_bytes_per_launch": fb + wb, "fetch_bytes_per_token": fb / per,
+               "write_bytes_per_token": wb / per, "traffic_bytes_per_token": (fb + wb) / per}
+        if alg_b:
+            ent["algorithmic_bytes_per_launch"] = alg_b
+            ent["traffic_over_algorithmic"] = (fb + wb) / alg_b
+        res[label] = ent
+    res["per_token"] = "per sequence-step" if "verify" not in bench else "per committed token"
+    if "replay_decode" in res:                 # the keys the headline bench line reads
+        res["algorithmic_bytes_per_launch"] = res["replay_decode"]["algorithmic_bytes_per_launch"]
+        res["traffic_bytes_per_launch"] = res["replay_decode"]["traffic_bytes_per_launch"]
+        res["traffic_over_algorithmic"] = res["replay_decode"]["traffic_over_algorithmic"]
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
     return res
@@ -902,13 +932,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the counter summary from two rocprofv3 --pmc runs and exit")
+                    help="write the counter summary of the bench run with these arguments (two rocprofv3 "
+                         "--pmc runs of it) and exit")
+    ap.add_argument("--counter-bench", help="the JSON line the FETCH_SIZE run printed (with --summarize-counters)")
+    ap.add_argument("--counter-out", default=PROFILE_SUMMARY, help="where the counter summary goes")
     ap.add_argument("--counter-command", default="", help="command recorded in the counter summary")
     args = ap.parse_args()
     if args.summarize_counters:
-        r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], PROFILE_SUMMARY,
-                               args.counter_command, args.batch or 256, args.steps, args.warmup, args.layers,
-                               args.reps)
+        from synth import get_workload
+        name = {"m2_verify_b512": "m2_verify_b512", "gdn_verify_b256": "gdn_b256",
+                "kda_verify_b256": "kda_b256"}.get(args.workload, args.workload)
+        wl = get_workload(name)
+        if args.batch:
+            wl = wl.replace(batch=args.batch)
+        if args.workload == "m2_readcopy_b256":
+            wl = wl.replace(read_copy=args.read_copy)
+        r = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.counter_out,
+                               args.counter_command, wl, args.counter_bench, args.steps, args.warmup,
+                               args.layers, args.reps)
         print(json.dumps(r, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
