@@ -346,60 +346,72 @@ __device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const u
   }
 }
 
-// Per-lane partial of S_read x from loaded read-copy registers.
+// Per-lane partial of S_read x from loaded read-copy registers.  Each 4-element slice of x
+// is read from LDS once and used for every row group of the lane (the lane's chunks are the
+// same columns in every row group).
 template <int N, int RGW>
 __device__ __forceinline__ void readcopy_dot(const RCopy<N, RGW> &R, int fmt, const float *x, int lane,
                                              float (&out)[RGW]) {
   const int c8 = lane & 7;
+  float acc[RGW];
 #pragma unroll
-  for (int i = 0; i < RGW; ++i) {
-    float acc = 0.f;
+  for (int i = 0; i < RGW; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
-      const int k = c8 + 8 * ci;
-      const bool has = k < RCopy<N, RGW>::NCH;   // lanes past the row's chunks contribute nothing
-      const float *xp = x + 16 * (has ? k : 0);
-      const uint4 w = has ? R.raw[i][ci] : make_uint4(0, 0, 0, 0);
-      const uint32_t sb = R.scb[i][ci];
-      // fp8: the fp32 scale; MXFP4: 2^(e8m0 - 127) is the e8m0 byte in the fp32 exponent field
-      const float sc = has ? __uint_as_float(fmt == RSSM_READ_FP8 ? sb : sb << 23) : 0.f;
-      if (fmt == RSSM_READ_FP8) {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        float d = 0.f;
+  for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
+    const int k = c8 + 8 * ci;
+    const bool has = k < RCopy<N, RGW>::NCH;   // lanes past the row's chunks contribute nothing
+    const float *xp = x + 16 * (has ? k : 0);
+    if (fmt == RSSM_READ_FP8) {
+      float d[RGW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws[q], 1.0f, false);
-          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws[q], 1.0f, true);
-          const float4 xv = *(const float4 *)(xp + 4 * q);
-          d = fmaf(lo[0], xv.x, d);
-          d = fmaf(lo[1], xv.y, d);
-          d = fmaf(hi[0], xv.z, d);
-          d = fmaf(hi[1], xv.w, d);
+      for (int i = 0; i < RGW; ++i) d[i] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 xv = *(const float4 *)(xp + 4 * q);
+#pragma unroll
+        for (int i = 0; i < RGW; ++i) {
+          const uint4 w = has ? R.raw[i][ci] : make_uint4(0, 0, 0, 0);
+          const uint32_t ws = q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w));
+          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws, 1.0f, false);
+          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ws, 1.0f, true);
+          d[i] = fmaf(lo[0], xv.x, d[i]);
+          d[i] = fmaf(lo[1], xv.y, d[i]);
+          d[i] = fmaf(hi[0], xv.z, d[i]);
+          d[i] = fmaf(hi[1], xv.w, d[i]);
         }
-        acc = fmaf(sc, d, acc);
-      } else {
-        const uint32_t ws[2] = {w.x, w.y};
+      }
+      // fp8: the fp32 block scale multiplies the chunk's dot product
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float4 xa = *(const float4 *)(xp + 8 * q);
-          const float4 xb = *(const float4 *)(xp + 8 * q + 4);
-          const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 0);
-          const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 1);
-          const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 2);
-          const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[q], sc, 3);
-          acc = fmaf(v0[0], xa.x, acc);
-          acc = fmaf(v0[1], xa.y, acc);
-          acc = fmaf(v1[0], xa.z, acc);
-          acc = fmaf(v1[1], xa.w, acc);
-          acc = fmaf(v2[0], xb.x, acc);
-          acc = fmaf(v2[1], xb.y, acc);
-          acc = fmaf(v3[0], xb.z, acc);
-          acc = fmaf(v3[1], xb.w, acc);
+      for (int i = 0; i < RGW; ++i) acc[i] = fmaf(has ? __uint_as_float(R.scb[i][ci]) : 0.f, d[i], acc[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float4 xa = *(const float4 *)(xp + 8 * q);
+        const float4 xb = *(const float4 *)(xp + 8 * q + 4);
+#pragma unroll
+        for (int i = 0; i < RGW; ++i) {
+          const uint4 w = has ? R.raw[i][ci] : make_uint4(0, 0, 0, 0);
+          const uint32_t ws = q == 0 ? w.x : w.y;
+          // MXFP4: 2^(e8m0 - 127) is the e8m0 byte in the fp32 exponent field
+          const float sc = has ? __uint_as_float(R.scb[i][ci] << 23) : 0.f;
+          const v2f v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws, sc, 0);
+          const v2f v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws, sc, 1);
+          const v2f v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws, sc, 2);
+          const v2f v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws, sc, 3);
+          acc[i] = fmaf(v0[0], xa.x, acc[i]);
+          acc[i] = fmaf(v0[1], xa.y, acc[i]);
+          acc[i] = fmaf(v1[0], xa.z, acc[i]);
+          acc[i] = fmaf(v1[1], xa.w, acc[i]);
+          acc[i] = fmaf(v2[0], xb.x, acc[i]);
+          acc[i] = fmaf(v2[1], xb.y, acc[i]);
+          acc[i] = fmaf(v3[0], xb.z, acc[i]);
+          acc[i] = fmaf(v3[1], xb.w, acc[i]);
         }
       }
     }
-    out[i] = acc;
   }
+#pragma unroll
+  for (int i = 0; i < RGW; ++i) out[i] = acc[i];
 }
 
 // ---------------------------------------------------------------- record staging
@@ -779,9 +791,32 @@ __device__ __forceinline__ float group_dot(const float *x, const float *y, int l
 __device__ __forceinline__ int small_div(int d, float inv_n) { return (int)(((float)d + 0.5f) * inv_n); }
 
 // Dot products k_j . q_tau for j < nrec, tau < T, by groups of 16 lanes -> coef[tau * cap + j].
+// With one query (decode) each lane keeps its slice of q in registers for all the records it
+// takes, so q is read from LDS once per lane instead of once per record.
 template <int N>
 __device__ void kq_dots(float *lds, const LdsLayout &L, int cap, int nrec, int T, int t) {
   const int g16 = t >> 4, l16 = t & 15;
+  if (T == 1) {
+    constexpr int NI = (N + 63) / 64;
+    float4 qv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = 4 * l16 + 64 * i;
+      qv[i] = n < N ? *(const float4 *)(lds + L.q + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int j = g16; j < nrec; j += kThreads / 16) {
+      const float *kr = lds + L.K + j * (N + 4);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = 4 * l16 + 64 * i;
+        if (n < N) acc = dot4(*(const float4 *)(kr + n), qv[i], acc);
+      }
+      acc = sum16(acc);
+      if (l16 == 0) lds[L.coef + j] = acc;
+    }
+    return;
+  }
   const float inv = 1.0f / (float)nrec;
   for (int d = g16; d < T * nrec; d += kThreads / 16) {
     const int tau = small_div(d, inv), j = d - tau * nrec;
