@@ -141,6 +141,16 @@ class ReplayOracle:
         delta = self.read_tol * np.max(np.abs(S), axis=(-2, -1), keepdims=True)
         return read_copy_ambiguity(self.wl.read_copy, S.astype(np.float32), delta)
 
+    def _read_copy_step(self, i: int, rec):
+        """Advance the read copy's chain by one committed record.  A non-flush output replays
+        every record committed since the last fold on top of the copy, whether it was
+        committed by a decode step or as an accepted draft."""
+        if self.R is None:
+            return
+        self.R[i], _ = step(self.wl.kind, self.R[i], rec)
+        if self.read_tol is not None:
+            self.Rgam[i] = self.Rgam[i] * rec["alpha"]
+
     def _checkpoint(self, i: int):
         self.S_ckpt[i] = self.S[i]
         if self.R is not None:
@@ -222,7 +232,9 @@ class ReplayOracle:
                 continue
             if self.track_state:
                 for t in range(a):
-                    self.S[i], _ = step(wl.kind, self.S[i], self._rec(self._drafts, i, t))
+                    rec = self._rec(self._drafts, i, t)
+                    self.S[i], _ = step(wl.kind, self.S[i], rec)
+                    self._read_copy_step(i, rec)
             self.n_committed[i] += a
 
     # -- tree-shaped drafts -------------------------------------------------------
@@ -298,7 +310,9 @@ class ReplayOracle:
                     for f in _FIELDS:
                         self.ring[f][i, (nc + j) % C] = recs[f][(nc + d) % C]
                 for d in chosen:
-                    self.S[i], _ = step(wl.kind, self.S[i], self._rec(self._drafts, i, d))
+                    rec = self._rec(self._drafts, i, d)
+                    self.S[i], _ = step(wl.kind, self.S[i], rec)
+                    self._read_copy_step(i, rec)
             self.n_committed[i] += a
 
     def flush(self, min_records: int):

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 from oracle import ReplayOracle, read_copy_dequant, replay_forms as rf, widen
-from synth import decode_inputs, get_workload, initial_state
+from synth import accept_counts, decode_inputs, draft_inputs, get_workload, initial_state
 
 
 def _wl(kind, fmt, dtype):
@@ -93,3 +93,55 @@ def test_read_copy_outputs_differ_from_the_fp32_outputs():
     inp = decode_inputs(wl, 0, seqs)
     y = orc.decode(inp)
     assert np.min(_rel(y, orc.y_exact)) > 1e-4
+
+
+def _recs_of(inp, i, dtype, t=None):
+    return {f: (None if inp[f] is None else widen(inp[f][i] if t is None else inp[f][i, t], dtype))
+            for f in ("alpha", "beta", "v", "k", "q")}
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
+def test_read_copy_window_holds_committed_drafts(kind, fmt):
+    """Accepted drafts join the window like decode records: after verify / commit rounds
+    with a per-sequence accepted prefix, every non-flush decode output is the replay form
+    over all records committed since the last fold (drafts and decode records, oldest
+    first) on the dequantised copy of the checkpoint."""
+    wl = _wl(kind, fmt, "bf16").replace(L=8, capacity=10, t_max=3)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    grp = wl.n_heads // wl.n_qk_heads
+    S_read = [read_copy_dequant(fmt, S0[i]) for i in seqs]
+    window = [[] for _ in seqs]
+    for r in range(2):                      # two rounds: up to 6 drafts, at most 7 records
+        d = draft_inputs(wl, r, seqs, 3)
+        orc.verify(d, 3)
+        acc = accept_counts(wl, r, 3)[: wl.batch]
+        acc[0] = 3                           # sequence 0 takes every draft
+        orc.commit(acc, 3)
+        for i in seqs:
+            window[i] += [_recs_of(d, i, wl.in_dtype, t)
+                          for t in range(int(acc[i]))]
+    assert not orc.err and len(window[0]) == 6
+    checked = 0
+    for t in range(10):
+        h_before = orc.h().copy()
+        inp = decode_inputs(wl, t, seqs)
+        y = orc.decode(inp)
+        for i in seqs:
+            rec = _recs_of(inp, i, wl.in_dtype)
+            window[i].append(rec)
+            if h_before[i] + 1 >= wl.L:        # fold step: a new copy of the new checkpoint
+                S_read[i] = read_copy_dequant(fmt, orc.S_ckpt[i].astype(np.float32))
+                window[i] = []
+                continue
+            for h in range(wl.n_heads):
+                g = h // grp
+                recs = [dict(alpha=x["alpha"][h], beta=None if x["beta"] is None else x["beta"][h],
+                             v=x["v"][h], k=x["k"][g]) for x in window[i]]
+                want = _window_output(kind, S_read[i][h], recs, rec["q"][g])
+                err = _rel(y[i, h], want)
+                assert err < 1e-12, f"step {t} seq {i} head {h}: {err:.3g}"
+                checked += 1
+    assert checked > 0 and not orc.err
