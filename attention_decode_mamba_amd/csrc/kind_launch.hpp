@@ -11,9 +11,51 @@ namespace launch_detail {
 inline dim3 grid_of(const Args &a) { return dim3((unsigned)(a.g.B * a.g.H)); }
 }  // namespace launch_detail
 
+// Mamba-2 decode with a read copy takes the one-wave-per-tile kernel where its layouts fit:
+// 16-byte record chunks, N of 64 or 128, P <= 64 (at most 8 row groups in one wave) and a
+// window of at most 16 records.
+template <int KIND, int STG>
+hipError_t decode_rc(const Args &a, hipStream_t s, bool *taken) {
+  *taken = false;
+  if constexpr (KIND == RSSM_KIND_MAMBA2 && STG != kStageScalar) {
+    const Geom &g = a.g;
+    if (g.read_copy == RSSM_READ_NONE || (g.N != 64 && g.N != 128) || g.P > 64 || g.L > 16) return hipSuccess;
+    *taken = true;
+    const int groups = (g.B + kWaves - 1) / kWaves * g.H;
+    const int wt = g.N == 64 ? WaveLds<64>::total : WaveLds<128>::total;
+    const size_t lds = (size_t)(decode_rc_flag_offset(g.C + 1, g.P, g.N, wt) + kWaves) * sizeof(float);
+#define CALL(n, r)                                                                               \
+  {                                                                                              \
+    hipLaunchKernelGGL((k_decode_rc<n, r, F, STG>), dim3((unsigned)groups), dim3(kThreads), lds, s, a); \
+    return hipGetLastError();                                                                    \
+  }
+#define RC_DISPATCH                                    \
+  switch (g.N * 10 + rgw_for(g.P)) {                   \
+    case 641: CALL(64, 1);                             \
+    case 642: CALL(64, 2);                             \
+    case 1281: CALL(128, 1);                           \
+    case 1282: CALL(128, 2);                           \
+    default: return hipErrorInvalidValue;              \
+  }
+    if (g.read_copy == RSSM_READ_FP8) {
+      constexpr int F = RSSM_READ_FP8;
+      RC_DISPATCH
+    } else {
+      constexpr int F = RSSM_READ_MXFP4;
+      RC_DISPATCH
+    }
+#undef RC_DISPATCH
+#undef CALL
+  }
+  return hipSuccess;
+}
+
 template <int KIND, int STG>
 hipError_t KindLaunch<KIND, STG>::decode(const Args &a, hipStream_t s) {
   using launch_detail::grid_of;
+  bool taken;
+  const hipError_t e = decode_rc<KIND, STG>(a, s, &taken);
+  if (taken) return e;
   const size_t lds = lds_bytes(KIND, a.g.C + 1, 1, a.g.P, a.g.N);
 #define CALL(n, r)                                                                             \
   {                                                                                            \

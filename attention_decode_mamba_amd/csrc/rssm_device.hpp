@@ -306,16 +306,17 @@ struct RCopy {
 
 // All loads are issued back to back: the format branch is outside the loops and nothing
 // is decoded here, so no load waits for another (decoding happens in readcopy_dot).
+// Row group i of the lane is row row0 + rstep * i.
 template <int N, int RGW>
-__device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const uint8_t *__restrict__ codes,
-                                              const uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
-                                              int lane) {
+__device__ __forceinline__ void readcopy_load_rows(RCopy<N, RGW> &R, int fmt, const uint8_t *__restrict__ codes,
+                                                   const uint8_t *__restrict__ scales, int64_t tile, int P,
+                                                   int row0, int rstep, int lane) {
   constexpr int NCH = RCopy<N, RGW>::NCH;
   const int c8 = lane & 7;
   if (fmt == RSSM_READ_FP8) {
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
-      int row = frag_row(wave, lane, i);
+      int row = row0 + rstep * i;
       row = row < P ? row : P - 1;               // ragged rows: a copy of row P - 1, never stored
       const int64_t rowi = tile * P + row;
 #pragma unroll
@@ -331,7 +332,7 @@ __device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const u
   } else {
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
-      int row = frag_row(wave, lane, i);
+      int row = row0 + rstep * i;
       row = row < P ? row : P - 1;
       const int64_t rowi = tile * P + row;
 #pragma unroll
@@ -344,6 +345,14 @@ __device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const u
       }
     }
   }
+}
+
+// The lane's rows in the row-octet layout of a 4-wave tile.
+template <int N, int RGW>
+__device__ __forceinline__ void readcopy_load(RCopy<N, RGW> &R, int fmt, const uint8_t *__restrict__ codes,
+                                              const uint8_t *__restrict__ scales, int64_t tile, int P, int wave,
+                                              int lane) {
+  readcopy_load_rows(R, fmt, codes, scales, tile, P, frag_row(wave, lane, 0), 8 * kWaves, lane);
 }
 
 // Per-lane partial of S_read x from loaded read-copy registers.  Each 4-element slice of x
@@ -1056,6 +1065,51 @@ constexpr int decode_min_waves() {
   return (KIND == RSSM_KIND_MAMBA2 && RCF != RSSM_READ_NONE && N >= 128 && RGW * N <= 256) ? 8 : 1;
 }
 
+// Record sources of a decode step: the hb window records from ring slot nk mod C on, then
+// the step's input record; the query is the step's input query.
+template <int KIND, int N>
+__device__ __forceinline__ StageSpec decode_spec(const Args &a, const LdsLayout &L, float *lds, int b, int hh, int gq,
+                                                 int64_t nk, int hb) {
+  const Geom &g = a.g;
+  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, 1, 1);
+  sp.ia0 = b * g.H + hh;
+  sp.iv0 = (b * g.H + hh) * g.P;
+  sp.ik0 = (b * g.G + gq) * N;
+  sp.iq0 = sp.ik0;
+  return sp;
+}
+
+// Fold step of one tile by the whole workgroup: the hb window records and the step's record
+// are folded into the checkpoint, which is written back with its read copy (format RCF), and
+// the output is read from the new checkpoint.  The caller advances the cursors.
+template <int KIND, int N, int RGW, int RCF, int STG>
+__device__ __forceinline__ void decode_fold_tile(const Args &a, float *lds, int tile, int64_t nk, int hb) {
+  constexpr int U = (KIND != RSSM_KIND_MAMBA2 || RGW > 2) ? 4 : 2;
+  const Geom &g = a.g;
+  const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int nrec = hb + 1, P = g.P, cap = g.C + 1;
+  const LdsLayout L = lds_layout(KIND, cap, 1, P, N);
+  float *tileS = a.s + (int64_t)tile * P * N;
+  const StageSpec sp = decode_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb);
+  float *yout = a.out + (b * g.H + hh) * P;
+  Frag<N, RGW> F;
+  stage_with_tile<U, KIND, STG>(sp, lds, t, [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
+  __syncthreads();
+  if (KIND == RSSM_KIND_MAMBA2) {
+    if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
+    __syncthreads();
+    fold_m2(F, lds, L, nrec, P, wave, lane);
+  } else {
+    fold_delta<KIND>(F, lds, L, nrec, P, wave, lane);
+  }
+  frag_store(F, tileS, P, wave, lane);
+  frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
+  float part[RGW];
+  frag_dot(F, lds + L.q, lane, part);
+  write_row_sums<RGW>(part, P, yout, wave, lane);
+}
+
 template <int KIND, int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) void k_decode(Args a) {
@@ -1079,35 +1133,15 @@ __attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) v
   const LdsLayout L = lds_layout(KIND, cap, 1, P, N);
   float *tileS = a.s + (int64_t)tile * P * N;
 
-  StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, 1, 1);
-  sp.ia0 = b * g.H + hh;
-  sp.iv0 = (b * g.H + hh) * P;
-  sp.ik0 = (b * g.G + gq) * N;
-  sp.iq0 = sp.ik0;
-
   // The fold step and the output-only step stage their records separately, so the tile
   // registers of one path are never live in the other (one shared allocation would have to
   // hold both).  The tile is streamed with nontemporal loads (read once per step; on a fold
   // step it is written back from registers).
   float *yout = a.out + (b * g.H + hh) * P;
   if (flush) {
-    Frag<N, RGW> F;
-    stage_with_tile<U, KIND, STG>(sp, lds, t,
-                                               [&]() { frag_load<N, RGW, true>(F, tileS, P, wave, lane); });
-    __syncthreads();
-    if (KIND == RSSM_KIND_MAMBA2) {
-      if (wave == 0) wave_decays(lds + L.alpha, nrec - 1, lds + L.dec, lds + L.gam, cap, lane);
-      __syncthreads();
-      fold_m2(F, lds, L, nrec, P, wave, lane);
-    } else {
-      fold_delta<KIND>(F, lds, L, nrec, P, wave, lane);
-    }
-    frag_store(F, tileS, P, wave, lane);
-    frag_store_read_copy<RCF>(F, a.s_read, a.s_read_scale, tile, P, wave, lane);
-    float part[RGW];
-    frag_dot(F, lds + L.q, lane, part);
-    write_row_sums<RGW>(part, P, yout, wave, lane);
+    decode_fold_tile<KIND, N, RGW, RCF, STG>(a, lds, tile, nk, hb);
   } else {
+    const StageSpec sp = decode_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb);
     Frag<N, RGW> F;
     RCopy<N, RGW> RCR;
     stage_with_tile<U, KIND, STG>(sp, lds, t, [&]() {
@@ -1141,6 +1175,279 @@ __attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) v
   if (t == 0) {
     a.n_committed[tile] = nc + 1;
     if (flush) a.n_ckpt[tile] = nc + 1;
+  }
+}
+
+// ================================================================ read-copy decode, one wave per tile
+// A non-fold Mamba-2 step served from the read copy moves a few KB per tile, so with a
+// 4-wave workgroup per tile the per-tile set-up (cursor, record addresses, staging,
+// barriers) costs more instruction issue than the arithmetic and the kernel is bound by
+// VALU issue, not HBM.  Here one wave takes one tile's non-fold step on its own, with no
+// workgroup barrier and no record staging: each lane loads the record pieces it works on
+// straight into registers.  A workgroup takes 4 tiles; those whose window is full are then
+// folded one after another by the whole workgroup with the fold of k_decode, so checkpoints,
+// read copies and fold-step outputs are bit-identical to it.
+
+// LDS of one wave's non-fold step (floats): the query (N), decays and k.q products of up to
+// 16 records, the per-record-group value sums (at most 64 lanes x 8 values) and the row
+// sums of the read-copy product (at most 64 rows).
+template <int N>
+struct WaveLds {
+  static constexpr int q = 0, dec = N, coef = N + 16, vt = N + 32, rc = N + 32 + 512, total = N + 32 + 512 + 64;
+};
+
+// LDS written by some lanes of a wave and read by other lanes of the same wave: a wave's LDS
+// operations complete in order, so only the compiler has to keep the reads after the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Floats of LDS of k_decode_rc: the fold step's layout or 4 waves' non-fold areas, whichever
+// is larger, then the 4 fold flags.
+__host__ __device__ inline int decode_rc_flag_offset(int cap, int P, int N, int wave_total) {
+  const int f = lds_layout(RSSM_KIND_MAMBA2, cap, 1, P, N).total;
+  const int w = kWaves * wave_total;
+  return up4(f > w ? f : w);
+}
+
+template <bool BF>
+__device__ __forceinline__ void widen(const uint4 w, float (&x)[BF ? 8 : 4]) {
+  if constexpr (BF) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(u[e] << 16);
+      x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  } else {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  }
+}
+
+// Non-fold decode step of one Mamba-2 tile by one wave (window of hb <= 14 records, so the
+// step sees nrec = hb + 1 <= 15 records; P <= 64; RG = 8-row groups covering P; RCR: the
+// tile's read copy, loaded in the row-octet layout with all row groups in this wave):
+//   y = G S_read q + sum_j dec_j (k_j . q) v_j,
+// dec_j = prod of alpha_m over j < m <= hb, G = prod of alpha_m over m <= hb (the output-only
+// replay of the window; the same quantities as the 4-wave step).  Lane layouts:
+// * decays: lane j holds record j;
+// * k . q: R lanes per record (R = min(16, key chunks)), each with CPL 16-byte chunks;
+// * sum_j w_j v_j: VC = P / (elements per chunk) lanes per record, each one chunk;
+// * read copy: the row-octet layout with all row groups in one wave.
+// Records past the window are clamped to the step's input record (their loads stay in
+// bounds) and contribute nothing.  The step's record is appended to ring slot
+// (nk + hb) mod C from registers (the input bits).
+template <int N, int RG, int RCF, bool BF>
+__device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG> &RCR, float *wl, int b, int hh,
+                                                int gq, int64_t nk, int hb, int lane) {
+  const Geom &g = a.g;
+  constexpr int es = BF ? 2 : 4, epc = 16 / es;
+  constexpr int KC = N / epc, R = KC < 16 ? KC : 16, CPL = KC / R, RPP = 64 / R;
+  constexpr int KP = (15 + RPP - 1) / RPP;   // key passes for up to 15 records
+  constexpr int VP = BF ? 2 : 4;             // value passes for up to 15 records at P <= 64
+  using W = WaveLds<N>;
+  static_assert(R == 8 || R == 16, "key rows of 8 or 16 chunks per record group");
+  const int P = g.P, C = g.C, nrec = hb + 1;
+  const int slot0 = ring_mod(nk, C);
+  const int hstr = g.B * g.H, kstr = g.B * g.G;
+  const int hrow = b * g.H + hh, krow = b * g.G + gq;
+  const uint8_t *rA = a.ring + g.off_alpha, *rV = a.ring + g.off_v, *rK = a.ring + g.off_k;
+  auto slot_of = [&](int j) {
+    const int s = slot0 + j;
+    return s >= C ? s - C : s;
+  };
+
+  // ---- loads: alpha, query, key rows, value rows (the read copy is in flight already)
+  uint32_t araw;
+  {
+    const int j = lane < hb ? lane : hb;
+    const size_t e = j < hb ? (size_t)slot_of(j) * hstr + hrow : (size_t)hrow;
+    const uint8_t *p = (j < hb ? rA : (const uint8_t *)a.alpha) + e * es;
+    araw = BF ? (uint32_t) * (const uint16_t *)p : *(const uint32_t *)p;
+  }
+  const int kr = lane / R, kc = lane % R;
+  const uint8_t *qrow = (const uint8_t *)a.q + (size_t)krow * N * es;
+  uint4 qraw[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) qraw[i] = *(const uint4 *)(qrow + (kc + R * i) * 16);
+  uint4 kraw[KP][CPL];
+#pragma unroll
+  for (int m = 0; m < KP; ++m) {
+    int j = kr + RPP * m;
+    j = j < hb ? j : hb;
+    const uint8_t *row = j < hb ? rK + ((size_t)slot_of(j) * kstr + krow) * N * es
+                                : (const uint8_t *)a.k + (size_t)krow * N * es;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) kraw[m][i] = *(const uint4 *)(row + (kc + R * i) * 16);
+  }
+  const int VC = P / epc, VR = 64 / VC;
+  const int vr = lane / VC, vc = lane - vr * VC;
+  uint4 vraw[VP];
+#pragma unroll
+  for (int m = 0; m < VP; ++m) {
+    int j = vr + VR * m;
+    j = j < hb ? j : hb;
+    const uint8_t *row = j < hb ? rV + ((size_t)slot_of(j) * hstr + hrow) * P * es
+                                : (const uint8_t *)a.v + (size_t)hrow * P * es;
+    vraw[m] = *(const uint4 *)(row + vc * 16);
+  }
+
+  // ---- decays (the suffix products of the 4-wave step)
+  const float al = BF ? __uint_as_float(araw << 16) : __uint_as_float(araw);
+  const float x = wave_suffix_product(lane < nrec ? al : 1.f, lane);
+  const float G = lane_value(x, 0);
+  const float nxt = __shfl_down(x, 1);
+  if (lane < nrec) wl[W::dec + lane] = lane < hb ? nxt : 1.f;
+
+  // ---- query: fp32 copy in LDS for the read-copy product, and k_j . q
+  float qf[CPL][epc];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) widen<BF>(qraw[i], qf[i]);
+  if (kr == 0) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int e = 0; e < epc; e += 4)
+        *(float4 *)(wl + W::q + (kc + R * i) * epc + e) = make_float4(qf[i][e], qf[i][e + 1], qf[i][e + 2], qf[i][e + 3]);
+  }
+#pragma unroll
+  for (int m = 0; m < KP; ++m) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      float kf[epc];
+      widen<BF>(kraw[m][i], kf);
+#pragma unroll
+      for (int e = 0; e < epc; ++e) acc = fmaf(kf[e], qf[i][e], acc);
+    }
+    acc = R == 16 ? sum16(acc) : oct_sum(acc);
+    const int j = kr + RPP * m;
+    if (kc == 0 && j < nrec) wl[W::coef + j] = acc;
+  }
+  wave_lds_sync();
+
+  // ---- sum_j w_j v_j: per-lane partial over the lane's records, then summed over the
+  // record groups through LDS
+  float vacc[epc];
+#pragma unroll
+  for (int e = 0; e < epc; ++e) vacc[e] = 0.f;
+#pragma unroll
+  for (int m = 0; m < VP; ++m) {
+    const int j = vr + VR * m;
+    if (vr < VR && j < nrec) {
+      const float w = wl[W::dec + j] * wl[W::coef + j];
+      float vf[epc];
+      widen<BF>(vraw[m], vf);
+#pragma unroll
+      for (int e = 0; e < epc; ++e) vacc[e] = fmaf(w, vf[e], vacc[e]);
+    }
+  }
+  if (vr < VR) {
+#pragma unroll
+    for (int e = 0; e < epc; e += 4)
+      *(float4 *)(wl + W::vt + vr * P + vc * epc + e) = make_float4(vacc[e], vacc[e + 1], vacc[e + 2], vacc[e + 3]);
+  }
+
+  // ---- S_read q, row sums to LDS (lane c8 of a row writes row group c8's sum)
+  float part[RG];
+  readcopy_dot(RCR, RCF, wl + W::q, lane, part);
+  const int r8 = lane >> 3, c8 = lane & 7;
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    const float sr = oct_sum(part[i]);
+    if (c8 == i) mine = sr;
+  }
+  const int row = 8 * c8 + r8;
+  if (c8 < RG && row < P) wl[W::rc + row] = mine;
+  wave_lds_sync();
+
+  // ---- output rows (lane p takes row p)
+  if (lane < P) {
+    float sv = 0.f;
+    for (int r = 0; r < VR; ++r) sv += wl[W::vt + r * P + lane];
+    a.out[(size_t)hrow * P + lane] = fmaf(G, wl[W::rc + lane], sv);
+  }
+
+  // ---- append the step's record (its input bits) to ring slot (nk + hb) mod C
+  const int sh = slot_of(hb);
+  if (lane == hb) {
+    uint8_t *p = a.ring + g.off_alpha + ((size_t)sh * hstr + hrow) * es;
+    if (BF)
+      *(uint16_t *)p = (uint16_t)araw;
+    else
+      *(uint32_t *)p = araw;
+  }
+#pragma unroll
+  for (int m = 0; m < VP; ++m)
+    if (vr < VR && vr + VR * m == hb)
+      *(uint4 *)(a.ring + g.off_v + ((size_t)sh * hstr + hrow) * P * es + vc * 16) = vraw[m];
+  if ((hh % g.grp) == 0) {           // key-head leader: key and query rows
+    uint8_t *kd = a.ring + g.off_k + ((size_t)sh * kstr + krow) * N * es;
+    uint8_t *qd = a.ring + g.off_q + ((size_t)sh * kstr + krow) * N * es;
+#pragma unroll
+    for (int m = 0; m < KP; ++m)
+      if (kr + RPP * m == hb)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) *(uint4 *)(kd + (kc + R * i) * 16) = kraw[m][i];
+    if (kr == 0)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) *(uint4 *)(qd + (kc + R * i) * 16) = qraw[i];
+  }
+}
+
+// Mamba-2 decode with a read copy: one wave per non-fold tile, then the fold tiles by the
+// whole workgroup (see above).  A workgroup takes one value head of 4 consecutive sequences:
+// sequences whose windows are at different positions fold at different steps, so a
+// workgroup rarely has more than one fold to run (4 heads of one sequence would always fold
+// together, and their workgroup would run 4 folds back to back).  The read copy is loaded
+// before the cursor arrives (on a fold step it goes unused).  Requires vector staging, N of
+// 64 or 128, P <= 64 and a window of at most 16 records.
+template <int N, int RGW, int RCF, int STG>
+__global__ __launch_bounds__(kThreads) void k_decode_rc(Args a) {
+  constexpr bool BF = STG == kStageBf16;
+  constexpr int RG = kWaves * RGW;
+  static_assert(STG != kStageScalar && RCF != RSSM_READ_NONE, "vector staging with a read copy");
+  extern __shared__ float lds[];
+  const Geom &g = a.g;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int grp = tile_of_block(((g.B + kWaves - 1) / kWaves) * g.H);
+  const int bq = grp / g.H, hh = grp - bq * g.H, gq = hh / g.grp;
+  const int b = bq * kWaves + wave;
+  const int tile = b * g.H + hh;
+  int *flags = (int *)(lds + decode_rc_flag_offset(g.C + 1, g.P, N, WaveLds<N>::total));
+  int fold = 0;
+  if (b < g.B) {
+    RCopy<N, RG> RCR;
+    readcopy_load_rows(RCR, RCF, a.s_read, a.s_read_scale, tile, g.P, lane >> 3, 8, lane);
+    const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
+    const int64_t hb64 = nc - nk;
+    if (hb64 < 0 || hb64 > g.C) {
+      if (lane == 0) atomicOr(a.err, RSSM_DEVERR_CURSOR);
+    } else if (hb64 + 1 >= g.L) {
+      fold = 1;
+    } else {
+      m2_nonfold_wave<N, RG, RCF, BF>(a, RCR, lds + wave * WaveLds<N>::total, b, hh, gq, nk, (int)hb64, lane);
+      if (lane == 0) a.n_committed[tile] = nc + 1;
+    }
+  }
+  if (lane == 0) flags[wave] = fold;
+  __syncthreads();
+  for (int w = 0; w < kWaves; ++w) {
+    if (!flags[w]) continue;               // the same for every thread of the workgroup
+    const int tw = (bq * kWaves + w) * g.H + hh;
+    const int64_t nc = a.n_committed[tw], nk = a.n_ckpt[tw];
+    decode_fold_tile<RSSM_KIND_MAMBA2, N, RGW, RCF, STG>(a, lds, tw, nk, (int)(nc - nk));
+    if (threadIdx.x == 0) {
+      a.n_committed[tw] = nc + 1;
+      a.n_ckpt[tw] = nc + 1;
+    }
+    __syncthreads();
   }
 }
 

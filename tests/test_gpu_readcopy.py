@@ -7,11 +7,12 @@ import torch
 
 from oracle import (ReplayOracle, dequantize_fp8_blocks, dequantize_mxfp4_blocks,
                     quantize_fp8_blocks, quantize_mxfp4_blocks)
-from synth import decode_inputs, get_workload, initial_state
+from synth import decode_inputs, draft_inputs, get_workload, initial_state
 from synth.stream import StepSource
 
-from gpu_util import (TOL, TOL_READ, decode, dev, new_state, read_copy_excess, relerr, tile_relerr,
-                      to_dev_inputs)
+from gpu_util import (TOL, TOL_READ, assert_counters, decode, dev, new_state, ptr, read_copy_excess, relerr,
+                      stream, tile_relerr, to_dev_inputs, verify)
+from attention_decode_mamba_amd import rssm as R
 from oracle_runs import READ_TOL, decode_runs
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +80,8 @@ def test_exact_readout_through_decode(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("shape", [(40, 64, "fp32"), (17, 32, "bf16"), (128, 128, "bf16")])
+@pytest.mark.parametrize("shape", [(40, 64, "fp32"), (17, 32, "bf16"), (128, 128, "bf16"), (64, 128, "bf16"),
+                                   (64, 128, "fp32"), (24, 128, "bf16"), (8, 64, "bf16"), (48, 128, "fp32")])
 def test_decode_with_read_copy_matches_oracle(fmt, shape):
     P, N, dt = shape
     wl = _wl(fmt, dv=P, dk=N, in_dtype=dt, L=6, capacity=6)
@@ -109,6 +111,69 @@ def test_decode_with_read_copy_matches_oracle(fmt, shape):
         if (t + 1) % wl.L == 0:
             assert tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max() <= TOL
     assert ds.error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_read_copy_decode_staggered_windows(fmt, dt):
+    """Mamba-2 read-copy decode at P = 64, N = 128 with a 16-record window, the shape served
+    with one tile per wave and one head of four sequences per workgroup: 5 sequences x 6
+    value heads over 3 key heads (the workgroups of sequence 4 hold one tile), windows
+    staggered by verify(T = 1) /
+    commit rounds (sequence b holds 3b mod 16 records) so that sequences fold at different
+    steps, then 40 decode steps.  Outputs against the oracle (fp32 tolerance plus the
+    quantisation ambiguity bound; fp8 also normwise); checkpoints bit-identical to the run
+    without a copy at every step, and so are a sequence's outputs at its fold steps; cursors;
+    the final read copy equal to the quantised final checkpoint."""
+    wl = _wl(fmt, batch=5, n_heads=6, n_qk_heads=3, dv=64, dk=128, in_dtype=dt, L=16, capacity=16, t_max=1)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0, read_tol=READ_TOL)
+    ds = new_state(wl, S0)
+    plain = new_state(wl.replace(read_copy="none"), S0)
+    o1 = torch.empty(wl.batch, 1, wl.n_heads, wl.dv, device="cuda")
+    for r in range(wl.L - 1):
+        d = draft_inputs(wl, 100 + r, seqs, 1)
+        dd = to_dev_inputs(d)
+        acc = np.array([1 if r < (3 * b) % wl.L else 0 for b in seqs], np.int32)
+        acc_d = dev(acc)                               # stays alive until the commits have run
+        for st in (ds, plain):
+            verify(st, 1, dd, o1)
+            R.rssm_commit(st.cfg, st.st, ptr(acc_d), 1, stream())
+        orc.verify(d, 1)
+        orc.commit(acc, 1)
+    assert_counters(ds, orc.n_committed, orc.n_ckpt, "after staggering")
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    folds = np.zeros(wl.batch, int)
+    for t in range(40):
+        fold = orc.h() + 1 >= wl.L
+        folds += fold
+        inp = decode_inputs(wl, t, seqs)
+        d = to_dev_inputs(inp)
+        decode(ds, d, y)
+        decode(plain, d, y2)
+        yr = orc.decode(inp)
+        got = y.cpu().numpy()
+        ex = read_copy_excess(got, yr, orc.allowance).max()
+        assert ex <= 0, f"step {t}: output outside fp32 tolerance + quantisation ambiguity by {ex:.3g}"
+        if fmt == "fp8":
+            assert relerr(got, yr).max() <= TOL_READ, f"step {t}"
+        assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32)), f"step {t}"
+        for b in np.nonzero(fold)[0]:
+            assert torch.equal(y[b].view(torch.int32), y2[b].view(torch.int32)), f"step {t} fold of sequence {b}"
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {t}")
+    assert folds.min() >= 2
+    codes, scales = ds.read_copy()
+    ck = ds.ckpt().cpu().numpy()
+    if fmt == "fp8":
+        rc, rs = quantize_fp8_blocks(ck)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    else:
+        rc, rs = quantize_mxfp4_blocks(ck)
+        assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert ds.error() == 0 and plain.error() == 0 and not orc.err
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
