@@ -13,13 +13,15 @@ inline dim3 grid_of(const Args &a) { return dim3((unsigned)(a.g.B * a.g.H)); }
 
 // Mamba-2 decode with a read copy takes the one-wave-per-tile kernel where its layouts fit:
 // 16-byte record chunks, N of 64 or 128, P <= 64 (at most 8 row groups in one wave) and a
-// window of at most 16 records.
+// window of 2 to 16 records (so the ring has at least 2 slots and each slot's rows lie
+// less than 4 GB apart).
 template <int KIND, int STG>
 hipError_t decode_rc(const Args &a, hipStream_t s, bool *taken) {
   *taken = false;
   if constexpr (KIND == RSSM_KIND_MAMBA2 && STG != kStageScalar) {
     const Geom &g = a.g;
-    if (g.read_copy == RSSM_READ_NONE || (g.N != 64 && g.N != 128) || g.P > 64 || g.L > 16) return hipSuccess;
+    if (g.read_copy == RSSM_READ_NONE || (g.N != 64 && g.N != 128) || g.P > 64 || g.L < 2 || g.L > 16)
+      return hipSuccess;
     *taken = true;
     const int groups = (g.B + kWaves - 1) / kWaves * g.H;
     const int wt = g.N == 64 ? WaveLds<64>::total : WaveLds<128>::total;

@@ -94,6 +94,23 @@ __device__ __forceinline__ float wave_suffix_product(float x, int lane) {
   return x;
 }
 
+// x_l <- prod_{m >= l} x_m within each DPP row of 16 lanes (lanes past the row count as 1).
+// For lanes 0..15 of a wave whose lanes 16..63 hold 1 this is bit-identical to
+// wave_suffix_product: the products are taken in the same order, and the steps that
+// wave_suffix_product adds past 16 lanes multiply by exactly 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_one(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_suffix_product(float x) {
+  x *= dpp_or_one<0x101>(x);      // row_shl:1 (lane l reads lane l + 1)
+  x *= dpp_or_one<0x102>(x);      // row_shl:2
+  x *= dpp_or_one<0x104>(x);      // row_shl:4
+  x *= dpp_or_one<0x108>(x);      // row_shl:8
+  return x;
+}
+
 // ---------------------------------------------------------------- fragments
 template <int N, int RGW>
 struct Frag {
@@ -313,35 +330,39 @@ __device__ __forceinline__ void readcopy_load_rows(RCopy<N, RGW> &R, int fmt, co
                                                    int row0, int rstep, int lane) {
   constexpr int NCH = RCopy<N, RGW>::NCH;
   const int c8 = lane & 7;
+  // The tile's codes and scales start at a workgroup-uniform address; rows are 32-bit
+  // offsets from it (a tile's read copy is far below 4 GB).
   if (fmt == RSSM_READ_FP8) {
+    const uint8_t *cb = codes + tile * P * N;
+    const uint8_t *sb = scales + tile * P * (N / 32) * 4;
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
       int row = row0 + rstep * i;
       row = row < P ? row : P - 1;               // ragged rows: a copy of row P - 1, never stored
-      const int64_t rowi = tile * P + row;
 #pragma unroll
       for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
         const int k = c8 + 8 * ci;
         const int kc = k < NCH ? k : NCH - 1;
-        const f4v v = __builtin_nontemporal_load((const f4v *)(codes + rowi * N + 16 * kc));
+        const f4v v = __builtin_nontemporal_load((const f4v *)(cb + (uint32_t)(row * N + 16 * kc)));
         R.raw[i][ci] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                                   __float_as_uint(v[3]));
-        R.scb[i][ci] = ((const uint32_t *)scales)[rowi * (N / 32) + kc / 2];
+        R.scb[i][ci] = *(const uint32_t *)(sb + (uint32_t)(row * (N / 32) * 4 + (kc / 2) * 4));
       }
     }
   } else {
+    const uint8_t *cb = codes + tile * P * (N / 2);
+    const uint8_t *sb = scales + tile * P * (N / 32);
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
       int row = row0 + rstep * i;
       row = row < P ? row : P - 1;
-      const int64_t rowi = tile * P + row;
 #pragma unroll
       for (int ci = 0; ci < RCopy<N, RGW>::CI; ++ci) {
         const int k = c8 + 8 * ci;
         const int kc = k < NCH ? k : NCH - 1;
-        const uint2 v = *(const uint2 *)(codes + rowi * (N / 2) + 8 * kc);
+        const uint2 v = *(const uint2 *)(cb + (uint32_t)(row * (N / 2) + 8 * kc));
         R.raw[i][ci] = make_uint4(v.x, v.y, 0, 0);
-        R.scb[i][ci] = scales[rowi * (N / 32) + kc / 2];
+        R.scb[i][ci] = sb[(uint32_t)(row * (N / 32) + kc / 2)];
       }
     }
   }
@@ -1254,34 +1275,42 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
   static_assert(R == 8 || R == 16, "key rows of 8 or 16 chunks per record group");
   const int P = g.P, C = g.C, nrec = hb + 1;
   const int slot0 = ring_mod(nk, C);
-  const int hstr = g.B * g.H, kstr = g.B * g.G;
   const int hrow = b * g.H + hh, krow = b * g.G + gq;
-  const uint8_t *rA = a.ring + g.off_alpha, *rV = a.ring + g.off_v, *rK = a.ring + g.off_k;
+  // Row addresses: slot s of the ring holds this head's rows at base + s * stride (strides
+  // are below 4 GB: a ring region holds fewer than 2^31 elements over C >= 2 slots).
+  const uint32_t ast = (uint32_t)(g.B * g.H) * es, vst = (uint32_t)(g.B * g.H) * P * es,
+                 kst = (uint32_t)(g.B * g.G) * N * es;
+  const uint8_t *ab = a.ring + g.off_alpha + (size_t)hrow * es;
+  const uint8_t *vb = a.ring + g.off_v + (size_t)hrow * P * es;
+  const uint8_t *kb = a.ring + g.off_k + (size_t)krow * N * es;
+  const uint8_t *qb = a.ring + g.off_q + (size_t)krow * N * es;
+  const uint8_t *ain = (const uint8_t *)a.alpha + (size_t)hrow * es;
+  const uint8_t *vin = (const uint8_t *)a.v + (size_t)hrow * P * es;
+  const uint8_t *kin = (const uint8_t *)a.k + (size_t)krow * N * es;
+  const uint8_t *qin = (const uint8_t *)a.q + (size_t)krow * N * es;
   auto slot_of = [&](int j) {
     const int s = slot0 + j;
-    return s >= C ? s - C : s;
+    return (uint32_t)(s >= C ? s - C : s);
   };
 
-  // ---- loads: alpha, query, key rows, value rows (the read copy is in flight already)
+  // ---- loads: alpha, query, key rows, value rows (the read copy is in flight already).
+  // Records past the window are clamped to the step's input record.
   uint32_t araw;
   {
     const int j = lane < hb ? lane : hb;
-    const size_t e = j < hb ? (size_t)slot_of(j) * hstr + hrow : (size_t)hrow;
-    const uint8_t *p = (j < hb ? rA : (const uint8_t *)a.alpha) + e * es;
+    const uint8_t *p = j < hb ? ab + (size_t)slot_of(j) * ast : ain;
     araw = BF ? (uint32_t) * (const uint16_t *)p : *(const uint32_t *)p;
   }
   const int kr = lane / R, kc = lane % R;
-  const uint8_t *qrow = (const uint8_t *)a.q + (size_t)krow * N * es;
   uint4 qraw[CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) qraw[i] = *(const uint4 *)(qrow + (kc + R * i) * 16);
+  for (int i = 0; i < CPL; ++i) qraw[i] = *(const uint4 *)(qin + (kc + R * i) * 16);
   uint4 kraw[KP][CPL];
 #pragma unroll
   for (int m = 0; m < KP; ++m) {
     int j = kr + RPP * m;
     j = j < hb ? j : hb;
-    const uint8_t *row = j < hb ? rK + ((size_t)slot_of(j) * kstr + krow) * N * es
-                                : (const uint8_t *)a.k + (size_t)krow * N * es;
+    const uint8_t *row = j < hb ? kb + (size_t)slot_of(j) * kst : kin;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) kraw[m][i] = *(const uint4 *)(row + (kc + R * i) * 16);
   }
@@ -1292,16 +1321,16 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
   for (int m = 0; m < VP; ++m) {
     int j = vr + VR * m;
     j = j < hb ? j : hb;
-    const uint8_t *row = j < hb ? rV + ((size_t)slot_of(j) * hstr + hrow) * P * es
-                                : (const uint8_t *)a.v + (size_t)hrow * P * es;
+    const uint8_t *row = j < hb ? vb + (size_t)slot_of(j) * vst : vin;
     vraw[m] = *(const uint4 *)(row + vc * 16);
   }
 
-  // ---- decays (the suffix products of the 4-wave step)
+  // ---- decays: lane j < nrec <= 15 holds record j; lanes past the window hold 1, so the
+  // 16-lane suffix product equals the one of the 4-wave step bit for bit
   const float al = BF ? __uint_as_float(araw << 16) : __uint_as_float(araw);
-  const float x = wave_suffix_product(lane < nrec ? al : 1.f, lane);
+  const float x = row_suffix_product(lane < nrec ? al : 1.f);
   const float G = lane_value(x, 0);
-  const float nxt = __shfl_down(x, 1);
+  const float nxt = dpp_or_one<0x101>(x);
   if (lane < nrec) wl[W::dec + lane] = lane < hb ? nxt : 1.f;
 
   // ---- query: fp32 copy in LDS for the read-copy product, and k_j . q
@@ -1353,6 +1382,32 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
       *(float4 *)(wl + W::vt + vr * P + vc * epc + e) = make_float4(vacc[e], vacc[e + 1], vacc[e + 2], vacc[e + 3]);
   }
 
+  // ---- append the step's record (its input bits) to ring slot (nk + hb) mod C before the
+  // read-copy product, so the record registers are free for it
+  const uint32_t sh = slot_of(hb);
+  if (lane == hb) {
+    uint8_t *p = (uint8_t *)ab + (size_t)sh * ast;
+    if (BF)
+      *(uint16_t *)p = (uint16_t)araw;
+    else
+      *(uint32_t *)p = araw;
+  }
+#pragma unroll
+  for (int m = 0; m < VP; ++m)
+    if (vr < VR && vr + VR * m == hb) *(uint4 *)((uint8_t *)vb + (size_t)sh * vst + vc * 16) = vraw[m];
+  if ((hh % g.grp) == 0) {           // key-head leader: key and query rows
+    uint8_t *kd = (uint8_t *)kb + (size_t)sh * kst;
+    uint8_t *qd = (uint8_t *)qb + (size_t)sh * kst;
+#pragma unroll
+    for (int m = 0; m < KP; ++m)
+      if (kr + RPP * m == hb)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) *(uint4 *)(kd + (kc + R * i) * 16) = kraw[m][i];
+    if (kr == 0)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) *(uint4 *)(qd + (kc + R * i) * 16) = qraw[i];
+  }
+
   // ---- S_read q, row sums to LDS (lane c8 of a row writes row group c8's sum)
   float part[RG];
   readcopy_dot(RCR, RCF, wl + W::q, lane, part);
@@ -1372,32 +1427,6 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
     float sv = 0.f;
     for (int r = 0; r < VR; ++r) sv += wl[W::vt + r * P + lane];
     a.out[(size_t)hrow * P + lane] = fmaf(G, wl[W::rc + lane], sv);
-  }
-
-  // ---- append the step's record (its input bits) to ring slot (nk + hb) mod C
-  const int sh = slot_of(hb);
-  if (lane == hb) {
-    uint8_t *p = a.ring + g.off_alpha + ((size_t)sh * hstr + hrow) * es;
-    if (BF)
-      *(uint16_t *)p = (uint16_t)araw;
-    else
-      *(uint32_t *)p = araw;
-  }
-#pragma unroll
-  for (int m = 0; m < VP; ++m)
-    if (vr < VR && vr + VR * m == hb)
-      *(uint4 *)(a.ring + g.off_v + ((size_t)sh * hstr + hrow) * P * es + vc * 16) = vraw[m];
-  if ((hh % g.grp) == 0) {           // key-head leader: key and query rows
-    uint8_t *kd = a.ring + g.off_k + ((size_t)sh * kstr + krow) * N * es;
-    uint8_t *qd = a.ring + g.off_q + ((size_t)sh * kstr + krow) * N * es;
-#pragma unroll
-    for (int m = 0; m < KP; ++m)
-      if (kr + RPP * m == hb)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) *(uint4 *)(kd + (kc + R * i) * 16) = kraw[m][i];
-    if (kr == 0)
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) *(uint4 *)(qd + (kc + R * i) * 16) = qraw[i];
   }
 }
 
