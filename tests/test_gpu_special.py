@@ -33,7 +33,9 @@ import torch
 from oracle import ReplayOracle
 from synth import accept_counts, get_workload, initial_state, special_decode_inputs, special_draft_inputs
 
-from gpu_util import TOL, assert_counters, decode, dev, new_state, ptr, stream, tile_relerr, to_dev_inputs, verify
+from gpu_util import (TOL, TOL_READ, assert_counters, decode, dev, new_state, ptr, stream, tile_relerr,
+                      to_dev_inputs, verify)
+from oracle_runs import READ_TOL
 from attention_decode_mamba_amd import rssm as R
 
 pytestmark = pytest.mark.gpu
@@ -110,3 +112,82 @@ def test_special_records(name, dtype):
         e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
         assert e <= TOL, f"verify step {s}: checkpoint rel err {e:.3g}"
     assert ds.error() == 0 and not orc.err
+
+
+def _excess(got, ref, allowance):
+    """read_copy_excess with the row scale floored like _err: alpha = 0 records leave rows
+    that are small against the call's largest, where fp32 rounding of the surviving terms
+    dominates."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    scale = np.maximum(scale, 1e-3 * max(float(scale.max()), 1e-30))
+    return np.abs(got - ref) - (TOL * scale + np.asarray(allowance) * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_special_records_read_copy(fmt, dtype):
+    """Special records through the Mamba-2 read-copy decode at the one-wave-per-tile shape
+    (P = 64, N = 128, 16-record window; 5 sequences x 4 heads over 2 key heads): two windows of
+    decode steps, then 12 rounds of verify(T = 4) / commit with the accepted prefix ~ U{0..4}
+    (every fourth round also a standalone flush of windows holding at least 8 records)
+    followed by three decode steps, so non-fold steps replay windows that hold committed drafts
+    and records with alpha in {0, 1}, unit and repeated keys and q = k.  Outputs against the
+    oracle (fp32 tolerance on the floored row scale of _err plus the oracle's quantisation
+    ambiguity bound; fp8 also normwise), cursors,
+    checkpoints bit-identical to a run without the copy, and against the oracle at every fold."""
+    wl = get_workload("m2_readcopy_b256").replace(name="special_rc", batch=5, n_heads=4, n_qk_heads=2, dv=64,
+                                                  dk=128, in_dtype=dtype, L=16, t_max=4, capacity=19,
+                                                  read_copy=fmt)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0, read_tol=READ_TOL)
+    ds = new_state(wl, S0)
+    plain = new_state(wl.replace(read_copy="none"), S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    o = torch.empty(wl.batch, wl.t_max, wl.n_heads, wl.dv, device="cuda")
+    step = [0]
+
+    def decode_step():
+        t = step[0]
+        step[0] += 1
+        inp = special_decode_inputs(wl, t, seqs)
+        d = to_dev_inputs(inp)
+        decode(ds, d, y)
+        decode(plain, d, y2)
+        yr = orc.decode(inp)
+        got = y.cpu().numpy()
+        ex = _excess(got, yr, orc.allowance).max()
+        assert ex <= 0, f"decode step {t}: outside fp32 tolerance + quantisation ambiguity by {ex:.3g}"
+        if fmt == "fp8":
+            assert _err(got, yr).max() <= TOL_READ, f"decode step {t}"
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"decode step {t}")
+        assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32)), f"decode step {t}"
+
+    for _ in range(2 * wl.L):
+        decode_step()
+    e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
+    assert e <= TOL, f"checkpoint rel err {e:.3g}"
+    T = wl.t_max
+    for r in range(12):
+        dr = special_draft_inputs(wl, 100 + r, seqs, T)
+        dd = to_dev_inputs(dr)
+        acc = accept_counts(wl, r, T)[: wl.batch]
+        acc_d = dev(acc)                          # device arguments stay alive until their kernels run
+        for st in (ds, plain):
+            verify(st, T, dd, o)
+            R.rssm_commit(st.cfg, st.st, ptr(acc_d), T, stream())
+        orc.verify(dr, T)
+        orc.commit(acc, T)
+        if r % 4 == 3:                            # a standalone flush of windows holding >= 8 records
+            for st in (ds, plain):
+                R.rssm_flush(st.cfg, st.st, 8, stream())
+            orc.flush(8)
+        for _ in range(3):                        # decode folds at h >= 15, so the next verify fits
+            decode_step()
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"round {r}")
+        e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
+        assert e <= TOL, f"round {r}: checkpoint rel err {e:.3g}"
+    assert ds.error() == 0 and plain.error() == 0 and not orc.err
