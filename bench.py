@@ -441,20 +441,44 @@ def run_decode(args, wl, with_conventional=True) -> dict:
     return res
 
 
+def decode_profile(wl) -> str:
+    """The counter summary under profiles/ that covers decode workload wl."""
+    if wl.read_copy != "none":
+        return os.path.join(ROOT, "profiles",
+                            f"k_decode_readcopy_{wl.read_copy}_mamba2_b256_h128_p64_n128_counters.txt")
+    return {"gdn_b256": os.path.join(ROOT, "profiles", "k_decode_gdn_b256_h32_p128_n128_counters.txt"),
+            "kda_b256": os.path.join(ROOT, "profiles", "k_decode_kda_b256_h32_p128_n128_counters.txt")}.get(
+                wl.name, PROFILE_SUMMARY)
+
+
+def decode_traffic(wl):
+    """HBM traffic per launch from the counter summary of wl, if it was taken from the current
+    kernel sources at this batch, workload and read-copy format; else None."""
+    path = decode_profile(wl)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    if (prof.get("kernel_source_hash") != kernel_source_hash() or prof.get("batch") != wl.batch
+            or prof.get("workload", WORKLOAD) != wl.name or prof.get("read_copy", "none") != wl.read_copy):
+        return None
+    return prof.get("traffic_bytes_per_launch")
+
+
+def decode_kernel_name(wl) -> str:
+    kind = {"mamba2": "mamba2", "gdn": "gdn", "kda": "kda"}[wl.kind]
+    if wl.read_copy != "none":
+        return f"k_decode_rc<mamba2, N={wl.dk}, read copy {wl.read_copy}>"
+    return f"k_decode<{kind}, N={wl.dk}, P={wl.dv}>"
+
+
 def headline(args) -> dict:
     from synth import get_workload
     wl = get_workload(WORKLOAD)
     if args.batch:
         wl = wl.replace(batch=args.batch)
     r = run_decode(args, wl)
-    traffic = None
-    if os.path.exists(PROFILE_SUMMARY):
-        with open(PROFILE_SUMMARY) as f:
-            prof = json.load(f)
-        if (prof.get("kernel_source_hash") == kernel_source_hash() and prof.get("batch") == wl.batch
-                and prof.get("workload", WORKLOAD) == WORKLOAD):
-            traffic = prof.get("traffic_bytes_per_launch")
-    r["roofline"]["traffic"] = traffic
+    r["roofline"]["traffic"] = decode_traffic(wl)
     r["roofline"]["kernel"] = "k_decode<mamba2, N=128, RGW=2>"
     out = {"metric": METRIC, "value": r.pop("value"), "unit": r.pop("unit"), "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r.pop("ms_per_step"),
@@ -988,6 +1012,8 @@ def main():
         if args.workload == "m2_readcopy_b256":
             wl = wl.replace(read_copy=args.read_copy)
         res = run_decode(args, wl)
+        res["roofline"]["traffic"] = decode_traffic(wl)
+        res["roofline"]["kernel"] = decode_kernel_name(wl)
         res["metric"] = f"replay decode tokens/s ({wl.name}, read copy {wl.read_copy})"
         res["config"] = {"workload": wl.name, "batch": wl.batch, "heads": wl.n_heads, "qk_heads": wl.n_qk_heads,
                          "dv": wl.dv, "dk": wl.dk, "window": wl.L, "read_copy": wl.read_copy}
