@@ -84,10 +84,13 @@ hipError_t KindLaunch<KIND, STG>::decode(const Args &a, hipStream_t s) {
 }
 
 // A fused fold (min_records > 0) writes the read copy in the state's format.
+// The verify gathers its output rows in LDS when that still fits the LDS budget.
 template <int KIND, int STG>
-hipError_t KindLaunch<KIND, STG>::verify(const Args &a, hipStream_t s) {
+hipError_t KindLaunch<KIND, STG>::verify(const Args &a0, hipStream_t s) {
   using launch_detail::grid_of;
-  const size_t lds = lds_bytes(KIND, a.g.C, a.T, a.g.P, a.g.N);
+  Args a = a0;
+  a.gather_out = lds_bytes(KIND, a.g.C, a.T, a.g.P, a.g.N, true) <= (size_t)kMaxLdsBytes;
+  const size_t lds = lds_bytes(KIND, a.g.C, a.T, a.g.P, a.g.N, a.gather_out);
 #define CALL(n, r)                                                                                   \
   {                                                                                                  \
     hipLaunchKernelGGL((k_verify<KIND, n, r, FOLD, F, STG>), grid_of(a), dim3(kThreads), lds, s, a); \

@@ -1508,7 +1508,7 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
   const bool fold = FOLD && hb >= a.min_records;
   const int P = g.P;
   const int cap = g.C;
-  const LdsLayout L = lds_layout(KIND, cap, T, P, N);
+  const LdsLayout L = lds_layout(KIND, cap, T, P, N, a.gather_out);
   float *tileS = a.s + (int64_t)tile * P * N;
 
   StageSpec sp = make_spec<KIND, N>(a, L, lds, b, hh, gq, nk, hb, T, T);
@@ -1591,12 +1591,33 @@ __global__ __launch_bounds__(kThreads) void k_verify(Args a) {
     xbase = lds + Lv.r;
   }
 
+  // Output rows: with a.gather_out they are collected in LDS and then stored as whole rows
+  // (16 bytes per lane where P and the output allow it) instead of 4 bytes per row-octet lane.
   for (int tau = 0; tau < T; ++tau) {
     float part[RGW];
     frag_dot(F, xbase + tau * N, lane, part);
-    float *orow = a.out + (((int64_t)b * T + tau) * g.H + hh) * P;
-    write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dec ? dec + tau * cap : nullptr, lds + Lv.coef + tau * cap,
-                    hv + tau + 1, P, orow, wave, lane);
+    const float *dt = dec ? dec + tau * cap : nullptr, *ct = lds + Lv.coef + tau * cap;
+    if (a.gather_out)                  // the same for every thread: LDS and global stores stay typed
+      write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dt, ct, hv + tau + 1, P, lds + L.o + tau * P, wave, lane);
+    else
+      write_rows<RGW>(part, lds[Lv.gam + tau], lds, Lv, dt, ct, hv + tau + 1, P,
+                      a.out + (((int64_t)b * T + tau) * g.H + hh) * P, wave, lane);
+  }
+  if (a.gather_out) {
+    __syncthreads();
+    float *ob = a.out + ((int64_t)b * T * g.H + hh) * P;     // row tau at ob + tau * H * P
+    if ((P & 3) == 0 && (((uintptr_t)a.out) & 15) == 0) {
+      const int P4 = P >> 2;
+      for (int c = t; c < T * P4; c += kThreads) {
+        const int tau = c / P4, e = c - tau * P4;
+        *(float4 *)(ob + (int64_t)tau * g.H * P + 4 * e) = *(const float4 *)(lds + L.o + tau * P + 4 * e);
+      }
+    } else {
+      for (int c = t; c < T * P; c += kThreads) {
+        const int tau = c / P, e = c - tau * P;
+        ob[(int64_t)tau * g.H * P + e] = lds[L.o + tau * P + e];
+      }
+    }
   }
   // Draft tau goes to slot (n_committed + tau) mod C, one wave per draft.  Draft slots are
   // never a committed record's slot (h + T <= C), so no sibling head's staging reads them.

@@ -50,6 +50,7 @@ struct Args {
   int T;                                   // drafts (verify / commit)
   int min_records;                         // flush threshold
   int vec16;                               // rows can be staged in 16-byte chunks
+  int gather_out;                          // verify: output rows gathered in LDS, stored whole
   int32_t *snap_cur;                       // snapshot path: committed slot per sequence [B]
   int snap_slots;                          // snapshot path: slots per sequence (t_max + 1)
 };
@@ -57,12 +58,13 @@ struct Args {
 // Float offsets of the per-workgroup LDS arrays.  cap = records staged, T = queries.
 // Rows of N floats (K, KDA's alpha) are padded by 4 floats.
 struct LdsLayout {
-  int alpha, beta, dec, coef, gam, misc, anc, q, r, K, V, total;
+  int alpha, beta, dec, coef, gam, misc, anc, q, r, K, V, o, total;
 };
 
 __host__ __device__ inline int up4(int x) { return (x + 3) & ~3; }
 
-__host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P, int N) {
+// out: T output rows of P floats at the end (verify with gathered output rows).
+__host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P, int N, bool out = false) {
   LdsLayout l;
   int o = 0;
   l.alpha = o; o += (kind == RSSM_KIND_KDA) ? cap * (N + 4) : up4(cap);   // KDA: an N-vector per record
@@ -76,12 +78,13 @@ __host__ __device__ inline LdsLayout lds_layout(int kind, int cap, int T, int P,
   l.r = o;     o += T * N;
   l.K = o;     o += cap * (N + 4);
   l.V = o;     o += up4(cap * P);
+  l.o = o;     o += out ? up4(T * P) : 0;
   l.total = o;
   return l;
 }
 
-inline size_t lds_bytes(int kind, int cap, int T, int P, int N) {
-  return (size_t)lds_layout(kind, cap, T, P, N).total * sizeof(float);
+inline size_t lds_bytes(int kind, int cap, int T, int P, int N, bool out = false) {
+  return (size_t)lds_layout(kind, cap, T, P, N, out).total * sizeof(float);
 }
 
 // Row groups of 8 handled per wave (the tile's P rows form ceil(P/8) groups over 4 waves),
