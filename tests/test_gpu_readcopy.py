@@ -244,3 +244,80 @@ def test_delta_rule_decode_with_read_copy(kind, fmt):
             assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
             assert tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max() <= TOL
     assert ds.error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("L", [2, 3])
+def test_read_copy_shortest_windows(fmt, L):
+    """The shortest windows through the one-wave read-copy decode (P = 64, N = 128, bf16): with
+    L = 2 every non-fold step replays only the step's own record over the copy, and every
+    other step folds.  Outputs against the oracle, checkpoints bit-identical to the run
+    without a copy, cursors."""
+    wl = _wl(fmt, dv=64, dk=128, in_dtype="bf16", L=L, capacity=L, batch=3, n_heads=4, n_qk_heads=2)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0, read_tol=READ_TOL)
+    ds = new_state(wl, S0)
+    plain = new_state(wl.replace(read_copy="none"), S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    for t in range(3 * L + 1):
+        inp = decode_inputs(wl, t, seqs)
+        d = to_dev_inputs(inp)
+        decode(ds, d, y)
+        decode(plain, d, y2)
+        yr = orc.decode(inp)
+        got = y.cpu().numpy()
+        assert read_copy_excess(got, yr, orc.allowance).max() <= 0, f"step {t}"
+        if fmt == "fp8":
+            assert relerr(got, yr).max() <= TOL_READ, f"step {t}"
+        assert torch.equal(ds.ckpt().view(torch.int32), plain.ckpt().view(torch.int32)), f"step {t}"
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {t}")
+    assert ds.error() == 0
+
+
+@pytest.mark.parametrize("fmt", ["none", "fp8", "mxfp4"])
+def test_decode_cursor_error_leaves_the_tile_untouched(fmt):
+    """Counters out of range on two tiles (n_ckpt past n_committed; a window longer than the
+    ring) set the device error bit and leave those tiles' cursors, output rows and checkpoints
+    untouched, over a non-fold step and a fold step of the others.  Every other tile, including
+    those that share a workgroup with a broken one in the read-copy kernel, matches a run
+    without the corruption bit for bit."""
+    wl = _wl(fmt, dv=64, dk=128, in_dtype="bf16", L=6, capacity=6, batch=3, n_heads=4, n_qk_heads=4)
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    ref = new_state(wl, S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    for t in range(3):
+        d = to_dev_inputs(decode_inputs(wl, t, seqs))
+        decode(ds, d, y)
+        decode(ref, d, y2)
+    nc, nk = ds.counters()
+    nk[1, 2] = nc[1, 2] + 1                       # h < 0
+    nc[2, 0] = nk[2, 0] + wl.capacity + 1         # h > C
+    bad = [(1, 2), (2, 0)]
+    keep_nc, keep_nk = nc.clone(), nk.clone()
+    keep_ck = ds.ckpt().clone()
+    good = torch.ones(wl.batch, wl.n_heads, dtype=torch.bool)
+    for b, h in bad:
+        good[b, h] = False
+    sentinel = torch.full_like(y, 12345.0)
+    for t in range(3, 6):                         # steps 3 and 4 are non-fold steps, step 5 folds
+        d = to_dev_inputs(decode_inputs(wl, t, seqs))
+        y.copy_(sentinel)
+        decode(ds, d, y)
+        decode(ref, d, y2)
+        torch.cuda.synchronize()
+        for b, h in bad:
+            assert torch.equal(y[b, h], sentinel[b, h]), f"step {t}: output row of broken tile ({b},{h}) written"
+            assert torch.equal(ds.ckpt()[b, h], keep_ck[b, h]), f"step {t}: checkpoint of ({b},{h}) changed"
+            assert int(nc[b, h]) == int(keep_nc[b, h]) and int(nk[b, h]) == int(keep_nk[b, h])
+        gy, ry = y.cpu()[good], y2.cpu()[good]
+        assert torch.equal(gy.view(torch.int32), ry.view(torch.int32)), f"step {t}: healthy outputs differ"
+        rc, rk = ref.counters()
+        assert torch.equal(nc.cpu()[good], rc.cpu()[good]) and torch.equal(nk.cpu()[good], rk.cpu()[good])
+        assert torch.equal(ds.ckpt().cpu()[good].view(torch.int32), ref.ckpt().cpu()[good].view(torch.int32))
+    assert ds.error() == R.RSSM_DEVERR_CURSOR
+    assert ref.error() == 0
