@@ -1436,7 +1436,7 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
 // workgroup rarely has more than one fold to run (4 heads of one sequence would always fold
 // together, and their workgroup would run 4 folds back to back).  The read copy is loaded
 // before the cursor arrives (on a fold step it goes unused).  Requires vector staging, N of
-// 64 or 128, P <= 64 and a window of at most 16 records.
+// 64 or 128, P <= 64 and a window of 2 to 16 records.
 template <int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_decode_rc(Args a) {
   constexpr bool BF = STG == kStageBf16;

@@ -48,10 +48,16 @@ KERNEL_SOURCES = ["attention_decode_mamba_amd/csrc/rssm_device.hpp",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources without their comments: a counter summary stays valid
+    across comment edits, which do not change the compiled kernels."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
