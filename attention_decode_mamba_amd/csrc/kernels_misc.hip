@@ -41,22 +41,41 @@ __global__ __launch_bounds__(kThreads) void k_commit_snapshot(Args a) {
   a.snap_cur[b] = ring_add(cur, acc, S);
 }
 
-// Tree commit, one workgroup per sequence: the accepted path's records (every head's
-// alpha, beta, v and every key head's k, q) move to the consecutive slots past the cursor,
-// then every head's cursor replica advances.  Record i goes from offset path[i] to offset
-// i; path[i] >= i, and a destination i is the source only of an entry j with path[j] = i,
-// which needs j <= i.  So moving the records in path order reads every source before it
-// is overwritten.
+// Workgroups per sequence of the tree commit: each takes a range of key heads and the value
+// heads that use them, about 8 KB of one record's rows, and at most 8 per sequence (Mamba-2
+// B=512 64x128: 8; KDA 128x128: 4; GDN 128x128: 2).
+__host__ __device__ inline int commit_tree_split(const Geom &g) {
+  const int es = g.bf16 ? 2 : 4;
+  const int64_t rec = (int64_t)g.H * (g.P + (g.kind == RSSM_KIND_KDA ? g.N : 1) + (g.kind != RSSM_KIND_MAMBA2 ? 1 : 0)) * es +
+                      (int64_t)2 * g.G * g.N * es;
+  int64_t s = rec / 8192;
+  s = s < 1 ? 1 : (s > 8 ? 8 : s);
+  return (int)(s < g.G ? s : g.G);
+}
+
+// Tree commit: the accepted path's records (every head's alpha, beta, v and every key
+// head's k, q) move to the consecutive slots past the cursor, then every head's cursor
+// replica advances.  Record i goes from offset path[i] to offset i; path[i] >= i, and a
+// destination i is the source only of an entry j with path[j] = i, which needs j <= i.  So
+// moving the records in path order reads every source before it is overwritten.
+// A sequence is split over commit_tree_split(g) workgroups by key-head range (one per
+// sequence left most of the GPU idle).  Each checks the path itself, reads the cursor
+// replica of its first value head, moves its heads' rows and advances its heads' cursors,
+// so no workgroup reads a cursor another one writes.
 __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
   __shared__ int s_path[kMaxDrafts], s_par[kMaxDrafts];
   __shared__ int s_ok;
   const Geom &g = a.g;
-  const int b = blockIdx.x;
+  const int H = g.H, G = g.G, P = g.P, N = g.N, C = g.C;
+  const int S = commit_tree_split(g), kpc = (G + S - 1) / S;
+  const int b = blockIdx.x / S, chunk = blockIdx.x - b * S;
+  const int g0 = chunk * kpc, g1 = g0 + kpc < G ? g0 + kpc : G;   // key heads [g0, g1)
+  if (g0 >= g1) return;                                          // the same for the workgroup
+  const int h0 = g0 * g.grp, h1 = g1 * g.grp;                    // their value heads
   const int t = threadIdx.x;
   const int T = a.T;
-  const int H = g.H, G = g.G, P = g.P, N = g.N, C = g.C;
   const size_t BH = (size_t)g.B * H, BG = (size_t)g.B * G;   // rows per ring slot
-  const int64_t nc = a.n_committed[(int64_t)b * H], nk = a.n_ckpt[(int64_t)b * H];
+  const int64_t nc = a.n_committed[(int64_t)b * H + h0], nk = a.n_ckpt[(int64_t)b * H + h0];
   const int64_t hb = nc - nk;
   if (hb < 0 || hb > C) {
     if (t == 0) atomicOr(a.err, RSSM_DEVERR_CURSOR);
@@ -101,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
     const int src = ring_add(slot0, s_path[i], C), dst = ring_add(slot0, i, C);
     // scalar alpha (Mamba-2, GDN) and beta (GDN, KDA) of every value head
     const int f0 = g.kind == RSSM_KIND_KDA ? 1 : 0, f1 = g.kind == RSSM_KIND_MAMBA2 ? 1 : 2;
-    for (int h = t; h < H; h += kThreads) {
+    for (int h = h0 + t; h < h1; h += kThreads) {
       const size_t hr = (size_t)b * H + h;
       for (int f = f0; f < f1; ++f) {
         const int64_t base = f == 0 ? g.off_alpha : g.off_beta;
@@ -111,41 +130,41 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
           *(uint32_t *)(a.ring + base + ((size_t)dst * BH + hr) * 4) = *(const uint32_t *)(a.ring + base + ((size_t)src * BH + hr) * 4);
       }
     }
-    // k and q of every key head: N * es is a multiple of 16 bytes for every dk
-    const int cpk = N * es / 16, nk2 = 2 * G * cpk;
+    // k and q of the key heads: N * es is a multiple of 16 bytes for every dk
+    const int ng = g1 - g0, cpk = N * es / 16, nk2 = 2 * ng * cpk;
     for (int c = t; c < nk2; c += kThreads) {
       const int row = c / cpk, part = c - row * cpk;          // cpk is a power of two
-      const int which = row >= G, gg = row - which * G;
+      const int which = row >= ng, gg = g0 + row - which * ng;
       const int64_t base = which ? g.off_q : g.off_k;
       const size_t kr = (size_t)b * G + gg;
       const uint8_t *ps = a.ring + base + ((size_t)src * BG + kr) * N * es + part * 16;
       uint8_t *pd = a.ring + base + ((size_t)dst * BG + kr) * N * es + part * 16;
       *(uint4 *)pd = *(const uint4 *)ps;
     }
-    // KDA: the alpha row (dk elements, a whole number of 16-byte chunks) of every value head
+    // KDA: the alpha row (dk elements, a whole number of 16-byte chunks) of the value heads
     if (g.kind == RSSM_KIND_KDA) {
-      const int cpa = N * es / 16, na = H * cpa;
+      const int cpa = N * es / 16, na = (h1 - h0) * cpa;
       for (int c = t; c < na; c += kThreads) {
-        const int h = c / cpa, part = c - h * cpa;
+        const int h = h0 + c / cpa, part = c % cpa;
         const size_t hr = (size_t)b * H + h;
         const uint8_t *ps = a.ring + g.off_alpha + ((size_t)src * BH + hr) * N * es + part * 16;
         uint8_t *pd = a.ring + g.off_alpha + ((size_t)dst * BH + hr) * N * es + part * 16;
         *(uint4 *)pd = *(const uint4 *)ps;
       }
     }
-    // v of every value head
+    // v of the value heads
     if (vec) {
-      const int cpv = P * es / 16, nvc = H * cpv;
+      const int cpv = P * es / 16, nvc = (h1 - h0) * cpv;
       for (int c = t; c < nvc; c += kThreads) {
-        const int h = g.cpv_lg >= 0 ? c >> g.cpv_lg : c / cpv, part = c - h * cpv;
+        const int hl = g.cpv_lg >= 0 ? c >> g.cpv_lg : c / cpv, part = c - hl * cpv, h = h0 + hl;
         const size_t hr = (size_t)b * H + h;
         const uint8_t *ps = a.ring + g.off_v + ((size_t)src * BH + hr) * P * es + part * 16;
         uint8_t *pd = a.ring + g.off_v + ((size_t)dst * BH + hr) * P * es + part * 16;
         *(uint4 *)pd = *(const uint4 *)ps;
       }
     } else {
-      for (int e = t; e < H * P; e += kThreads) {
-        const int h = e / P, pp = e - h * P;
+      for (int e = t; e < (h1 - h0) * P; e += kThreads) {
+        const int h = h0 + e / P, pp = e % P;
         const size_t hr = (size_t)b * H + h;
         const size_t os = g.off_v + (((size_t)src * BH + hr) * P + pp) * es, od = g.off_v + (((size_t)dst * BH + hr) * P + pp) * es;
         if (es == 2)
@@ -155,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_commit_tree(Args a) {
       }
     }
   }
-  for (int h = t; h < H; h += kThreads) a.n_committed[(int64_t)b * H + h] = nc + acc;
+  for (int h = h0 + t; h < h1; h += kThreads) a.n_committed[(int64_t)b * H + h] = nc + acc;
 }
 
 __global__ void k_clear_err(int32_t *err) {
@@ -186,7 +205,7 @@ hipError_t launch_commit(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_commit_tree(const Args &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_commit_tree, dim3((unsigned)a.g.B), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(k_commit_tree, dim3((unsigned)(a.g.B * commit_tree_split(a.g))), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
