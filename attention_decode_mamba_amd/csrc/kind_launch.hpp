@@ -26,6 +26,10 @@ hipError_t decode_rc(const Args &a, hipStream_t s, bool *taken) {
     const int groups = (g.B + kWaves - 1) / kWaves * g.H;
     const int wt = g.N == 64 ? WaveLds<64>::total : WaveLds<128>::total;
     const size_t lds = (size_t)(decode_rc_flag_offset(g.C + 1, g.P, g.N, wt) + kWaves) * sizeof(float);
+    if (lds > (size_t)kMaxLdsBytes) {            // the flags past a fold layout at the budget's edge
+      *taken = false;
+      return hipSuccess;
+    }
 #define CALL(n, r)                                                                               \
   {                                                                                              \
     hipLaunchKernelGGL((k_decode_rc<n, r, F, STG>), dim3((unsigned)groups), dim3(kThreads), lds, s, a); \
