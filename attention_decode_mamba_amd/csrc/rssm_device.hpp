@@ -1233,6 +1233,8 @@ __host__ __device__ inline int decode_rc_flag_offset(int cap, int P, int N, int 
   return up4(f > w ? f : w);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <bool BF>
 __device__ __forceinline__ void widen(const uint4 w, float (&x)[BF ? 8 : 4]) {
   if constexpr (BF) {
@@ -1314,8 +1316,10 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
 #pragma unroll
     for (int i = 0; i < CPL; ++i) kraw[m][i] = *(const uint4 *)(row + (kc + R * i) * 16);
   }
-  const int VC = P / epc, VR = 64 / VC;
-  const int vr = lane / VC, vc = lane - vr * VC;
+  // VC lanes per value row; a power of two (the common case) takes shifts, not divisions
+  const int lg = g.cpv_lg;
+  const int VC = lg >= 0 ? 1 << lg : P / epc, VR = lg >= 0 ? 64 >> lg : 64 / VC;
+  const int vr = lg >= 0 ? lane >> lg : lane / VC, vc = lane - vr * VC;
   uint4 vraw[VP];
 #pragma unroll
   for (int m = 0; m < VP; ++m) {
@@ -1349,10 +1353,21 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      float kf[epc];
-      widen<BF>(kraw[m][i], kf);
+      if constexpr (BF) {
+        // bf16 pairs straight from the loaded bits: each product of two bf16 values is exact
+        // in fp32, so only the accumulation rounds (as in the FMA form, in another order)
+        const uint32_t kw[4] = {kraw[m][i].x, kraw[m][i].y, kraw[m][i].z, kraw[m][i].w};
+        const uint32_t qw[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
-      for (int e = 0; e < epc; ++e) acc = fmaf(kf[e], qf[i][e], acc);
+        for (int e = 0; e < 4; ++e)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]), __builtin_bit_cast(bf16x2, qw[e]),
+                                                acc, false);
+      } else {
+        float kf[epc];
+        widen<BF>(kraw[m][i], kf);
+#pragma unroll
+        for (int e = 0; e < epc; ++e) acc = fmaf(kf[e], qf[i][e], acc);
+      }
     }
     acc = R == 16 ? sum16(acc) : oct_sum(acc);
     const int j = kr + RPP * m;
