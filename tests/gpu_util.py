@@ -92,3 +92,19 @@ def read_copy_excess(got, ref, allowance):
     ref = np.asarray(ref, np.float64)
     scale = np.max(np.abs(ref), axis=-1, keepdims=True)
     return np.abs(got - ref) - (TOL * scale + np.asarray(allowance) * (1 + 1e-9))
+
+
+def check_ring(ds, orc, seqs):
+    """Every live ring slot of the device state holds the oracle's record bits (alpha, v and
+    beta per value head; k and q per key head)."""
+    ring = {k: (None if v is None else ring_bits(v)) for k, v in ds.ring_arrays().items()}
+    wl = orc.wl
+    for i, b in enumerate(seqs):
+        for slot in orc.live_slots(i):
+            assert np.array_equal(ring["alpha"][b, :, slot], orc.ring["alpha"][i, slot])
+            assert np.array_equal(ring["v"][b, :, slot], orc.ring["v"][i, slot])
+            g_lead = np.arange(wl.n_qk_heads)
+            assert np.array_equal(ring["k"][b, g_lead, slot], orc.ring["k"][i, slot])
+            assert np.array_equal(ring["q"][b, g_lead, slot], orc.ring["q"][i, slot])
+            if ring["beta"] is not None:
+                assert np.array_equal(ring["beta"][b, :, slot], orc.ring["beta"][i, slot])

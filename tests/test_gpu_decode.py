@@ -9,28 +9,14 @@ from oracle import ReplayOracle
 from synth import decode_inputs, draft_inputs, get_workload, initial_state
 from synth.stream import StepSource
 
-from gpu_util import (TOL, assert_counters, decode, dev, new_state, ptr, relerr, ring_bits, stream,
+from gpu_util import (TOL, assert_counters, check_ring, decode, dev, new_state, ptr, relerr, stream,
                       tile_relerr, to_dev_inputs, verify)
 from oracle_runs import cursor_run, decode_runs
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_ring(ds, orc, seqs):
-    ring = {k: (None if v is None else ring_bits(v)) for k, v in ds.ring_arrays().items()}
-    wl = orc.wl
-    for i, b in enumerate(seqs):
-        for slot in orc.live_slots(i):
-            assert np.array_equal(ring["alpha"][b, :, slot], orc.ring["alpha"][i, slot])
-            assert np.array_equal(ring["v"][b, :, slot], orc.ring["v"][i, slot])
-            g_lead = np.arange(wl.n_qk_heads)
-            assert np.array_equal(ring["k"][b, g_lead, slot], orc.ring["k"][i, slot])
-            assert np.array_equal(ring["q"][b, g_lead, slot], orc.ring["q"][i, slot])
-            if ring["beta"] is not None:
-                assert np.array_equal(ring["beta"][b, :, slot], orc.ring["beta"][i, slot])
-
-
-def _run_small(wl, steps, check_ring=True):
+def _run_small(wl, steps, ring=True):
     seqs = list(range(wl.batch))
     S0 = initial_state(wl, seqs)
     orc = ReplayOracle(wl, seqs, S0)
@@ -49,8 +35,8 @@ def _run_small(wl, steps, check_ring=True):
         if np.all(orc.n_ckpt == orc.n_committed):
             e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
             assert e <= TOL, f"step {t}: checkpoint rel err {e:.3g}"
-        if check_ring:
-            _check_ring(ds, orc, seqs)
+        if ring:
+            check_ring(ds, orc, seqs)
     assert ds.error() == 0
     return np.array(ys)
 
@@ -64,8 +50,8 @@ def test_tiny_mamba2_decode(s0):
 
 def test_tiny_mamba2_decode_deterministic():
     wl = get_workload("m2_tiny")
-    a = _run_small(wl, 20, check_ring=False)
-    b = _run_small(wl, 20, check_ring=False)
+    a = _run_small(wl, 20, ring=False)
+    b = _run_small(wl, 20, ring=False)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
@@ -90,6 +76,18 @@ SHAPES = [
     ("gdn", "fp32", 2, 2, 1, 512, 32, 4, 4),
     ("kda", "bf16", 2, 2, 2, 500, 32, 4, 4),
     ("mamba2", "fp32", 2, 2, 2, 256, 64, 4, 4),
+    # H a multiple of 16: Mamba-2 and KDA append each group of 16 heads from the group's last
+    # workgroup, dispatched after all others (ragged grids; 8 x 16 tiles take the XCD order;
+    # key groups of 8 and of 3 heads; fp32 rows; rows not 16-byte aligned; GDN keeps per-tile
+    # appends)
+    ("mamba2", "bf16", 3, 16, 16, 16, 32, 4, 4),
+    ("mamba2", "bf16", 8, 16, 16, 64, 128, 5, 5),
+    ("mamba2", "fp32", 2, 32, 4, 8, 32, 3, 3),
+    ("mamba2", "bf16", 2, 48, 16, 8, 32, 3, 3),
+    ("kda", "bf16", 2, 16, 8, 40, 64, 4, 4),
+    ("kda", "bf16", 3, 16, 16, 33, 32, 3, 3),
+    ("kda", "fp32", 8, 16, 16, 16, 32, 3, 3),
+    ("gdn", "bf16", 2, 16, 8, 16, 32, 4, 4),
 ]
 
 _BASE = {"mamba2": "m2_tiny", "gdn": "gdn_b256", "kda": "kda_b256"}
@@ -104,15 +102,17 @@ def test_decode_shapes_and_ragged_tails(shape):
     _run_small(wl, 3 * L + 3)
 
 
-@pytest.mark.parametrize("kind,L", [("mamba2", 4), ("mamba2", 16), ("gdn", 8), ("kda", 8)])
-def test_staggered_windows_decode(kind, L):
+@pytest.mark.parametrize("kind,L,H,G", [("mamba2", 4, 3, 3), ("mamba2", 16, 3, 3), ("gdn", 8, 4, 2), ("kda", 8, 4, 2),
+                                         ("mamba2", 8, 16, 16), ("kda", 4, 16, 8)])
+def test_staggered_windows_decode(kind, L, H, G):
     """Windows at different phases: sequence b first commits b mod L one-draft verifies
     (verify(T=1) + commit(0 or 1)), so each decode step folds only the sequences whose window
-    fills on that step.  Every output, cursor and checkpoint against the oracle for 2L steps."""
+    fills on that step.  Every output, cursor and checkpoint against the oracle for 2L steps,
+    and every live ring slot bit for bit (with 16 heads the appends of a sequence's group of 16
+    heads come from its last workgroup, which skips them when the sequence folds)."""
     base = get_workload(_BASE[kind])
-    wl = base.replace(name="stagger", batch=2 * L + 1, n_heads=3 if kind == "mamba2" else 4,
-                      n_qk_heads=3 if kind == "mamba2" else 2, dv=24, dk=64, in_dtype="bf16", L=L, t_max=1,
-                      capacity=L, read_copy="none")
+    wl = base.replace(name="stagger", batch=2 * L + 1, n_heads=H, n_qk_heads=G, dv=24, dk=64, in_dtype="bf16",
+                      L=L, t_max=1, capacity=L, read_copy="none")
     seqs = list(range(wl.batch))
     S0 = initial_state(wl, seqs)
     orc = ReplayOracle(wl, seqs, S0)
@@ -142,6 +142,7 @@ def test_staggered_windows_decode(kind, L):
         assert 1 <= int(folded.sum()) <= 3           # b mod L hits each phase 2 or 3 times
         e = tile_relerr(ds.ckpt().cpu().numpy()[folded], orc.S_ckpt[folded]).max()
         assert e <= TOL, f"step {t}: checkpoint rel err {e:.3g}"
+        check_ring(ds, orc, seqs)
     assert ds.error() == 0
 
 
@@ -208,3 +209,70 @@ def test_serving_shape_decode_sampled():
                       flush=True)
     assert worst <= TOL and worst_c <= TOL
     assert ds.error() == 0
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "kda"])
+def test_decode_cursor_error_with_group_appends(kind):
+    """With 16 value heads the ring appends of a group of 16 heads of a sequence come from the
+    workgroup of its last head.  A broken main tile (1, 2) is left out of its group's appends:
+    its cursors, output rows, checkpoint and ring rows stay untouched, and the rest of sequence
+    1 matches a run without the corruption bit for bit, ring included.  A broken appender
+    (2, 15) sets the error bit and stays untouched; its group's other heads still produce the
+    step's outputs, but their records of that step are not appended.  Sequence 0 matches the
+    clean run bit for bit throughout."""
+    base = get_workload("m2_decode_b256" if kind == "mamba2" else "kda_b256")
+    wl = base.replace(name="group_err", batch=3, n_heads=16, n_qk_heads=16, dv=64 if kind == "mamba2" else 32,
+                      dk=128 if kind == "mamba2" else 64, in_dtype="bf16", L=6, capacity=6, t_max=1,
+                      read_copy="none")
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    ds = new_state(wl, S0)
+    ref = new_state(wl, S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    y2 = torch.empty_like(y)
+    for t in range(3):
+        d = to_dev_inputs(decode_inputs(wl, t, seqs))
+        decode(ds, d, y)
+        decode(ref, d, y2)
+    nc, nk = ds.counters()
+    nk[1, 2] = nc[1, 2] + 1                       # h < 0 on a main tile
+    nc[2, 15] = nk[2, 15] + wl.capacity + 1       # h > C on an appender
+    bad = [(1, 2), (2, 15)]
+    keep_nc, keep_nk = nc.clone(), nk.clone()
+    keep_ck = ds.ckpt().clone()
+    ring0 = {k: (None if v is None else v.clone()) for k, v in ds.ring_arrays().items()}
+    good = torch.ones(wl.batch, wl.n_heads, dtype=torch.bool)
+    good[1, 2] = False
+    good[2, :] = False                            # the broken appender's group
+    sentinel = torch.full_like(y, 12345.0)
+    for t in range(3, 6):                         # steps 3 and 4 are non-fold steps, step 5 folds
+        d = to_dev_inputs(decode_inputs(wl, t, seqs))
+        y.copy_(sentinel)
+        decode(ds, d, y)
+        decode(ref, d, y2)
+        torch.cuda.synchronize()
+        for b, h in bad:
+            assert torch.equal(y[b, h], sentinel[b, h]), f"step {t}: output row of broken tile ({b},{h}) written"
+            assert torch.equal(ds.ckpt()[b, h], keep_ck[b, h]), f"step {t}: checkpoint of ({b},{h}) changed"
+            assert int(nc[b, h]) == int(keep_nc[b, h]) and int(nk[b, h]) == int(keep_nk[b, h])
+        ring = ds.ring_arrays()
+        for name in ("alpha", "v", "beta"):
+            if ring[name] is not None:
+                assert torch.equal(ring[name][1, 2], ring0[name][1, 2]), f"step {t}: ring {name} of (1,2) written"
+        for name in ("k", "q"):
+            assert torch.equal(ring[name][1, 2], ring0[name][1, 2]), f"step {t}: ring {name} of key head 2 written"
+        gy, ry = y.cpu()[good], y2.cpu()[good]
+        assert torch.equal(gy.view(torch.int32), ry.view(torch.int32)), f"step {t}: healthy outputs differ"
+        if t == 3:                                # the group's records up to step 2 were appended
+            assert torch.equal(y[2, :15].cpu().view(torch.int32), y2[2, :15].cpu().view(torch.int32))
+        rc, rk = ref.counters()
+        assert torch.equal(nc.cpu()[good], rc.cpu()[good]) and torch.equal(nk.cpu()[good], rk.cpu()[good])
+        assert torch.equal(ds.ckpt().cpu()[good].view(torch.int32), ref.ckpt().cpu()[good].view(torch.int32))
+        rr = ref.ring_arrays()
+        for name in ("alpha", "v", "beta"):
+            if ring[name] is not None:
+                assert torch.equal(ring[name].cpu()[good], rr[name].cpu()[good]), f"step {t}: ring {name} differs"
+        for name in ("k", "q"):                   # key head g is led by value head g (G = H)
+            assert torch.equal(ring[name].cpu()[good], rr[name].cpu()[good]), f"step {t}: ring {name} differs"
+    assert ds.error() == R.RSSM_DEVERR_CURSOR
+    assert ref.error() == 0

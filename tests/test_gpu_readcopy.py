@@ -10,8 +10,8 @@ from oracle import (ReplayOracle, dequantize_fp8_blocks, dequantize_mxfp4_blocks
 from synth import decode_inputs, draft_inputs, get_workload, initial_state
 from synth.stream import StepSource
 
-from gpu_util import (TOL, TOL_READ, assert_counters, decode, dev, new_state, ptr, read_copy_excess, relerr,
-                      stream, tile_relerr, to_dev_inputs, verify)
+from gpu_util import (TOL, TOL_READ, assert_counters, check_ring, decode, dev, new_state, ptr, read_copy_excess,
+                      relerr, stream, tile_relerr, to_dev_inputs, verify)
 from attention_decode_mamba_amd import rssm as R
 from oracle_runs import READ_TOL, decode_runs
 
@@ -114,8 +114,8 @@ def test_decode_with_read_copy_matches_oracle(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("dt", ["bf16", "fp32"])
-def test_read_copy_decode_staggered_windows(fmt, dt):
+@pytest.mark.parametrize("dt,H,G", [("bf16", 6, 3), ("fp32", 6, 3), ("bf16", 16, 16), ("bf16", 32, 8)])
+def test_read_copy_decode_staggered_windows(fmt, dt, H, G):
     """Mamba-2 read-copy decode at P = 64, N = 128 with a 16-record window, the shape served
     with one tile per wave and one head of four sequences per workgroup: 5 sequences x 6
     value heads over 3 key heads (the workgroups of sequence 4 hold one tile), windows
@@ -124,8 +124,10 @@ def test_read_copy_decode_staggered_windows(fmt, dt):
     steps, then 40 decode steps.  Outputs against the oracle (fp32 tolerance plus the
     quantisation ambiguity bound; fp8 also normwise); checkpoints bit-identical to the run
     without a copy at every step, and so are a sequence's outputs at its fold steps; cursors;
-    the final read copy equal to the quantised final checkpoint."""
-    wl = _wl(fmt, batch=5, n_heads=6, n_qk_heads=3, dv=64, dk=128, in_dtype=dt, L=16, capacity=16, t_max=1)
+    every live ring slot bit for bit (also at 16 and 32 heads, where the decode on the fp32
+    tile appends each group of 16 heads from its last workgroup); the final read copy equal to
+    the quantised final checkpoint."""
+    wl = _wl(fmt, batch=5, n_heads=H, n_qk_heads=G, dv=64, dk=128, in_dtype=dt, L=16, capacity=16, t_max=1)
     seqs = list(range(wl.batch))
     S0 = initial_state(wl, seqs)
     orc = ReplayOracle(wl, seqs, S0, read_tol=READ_TOL)
@@ -163,6 +165,7 @@ def test_read_copy_decode_staggered_windows(fmt, dt):
         for b in np.nonzero(fold)[0]:
             assert torch.equal(y[b].view(torch.int32), y2[b].view(torch.int32)), f"step {t} fold of sequence {b}"
         assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {t}")
+        check_ring(ds, orc, seqs)
     assert folds.min() >= 2
     codes, scales = ds.read_copy()
     ck = ds.ckpt().cpu().numpy()
