@@ -952,12 +952,38 @@ __device__ __forceinline__ void fold_m2(Frag<N, RGW> &F, const float *lds, const
 
 // Gated DeltaNet fold, one delta-rule update per record in registers:
 // S <- a S ; u = b (v - S k) ; S <- S + u k^T.
+// The tile is held as S = s F with one scalar s, the product of the decays since the last
+// rescale, so a record costs one FMA per element for S k and one for the rank-1 update:
+//   s' = s a ; w = s' (F k) ; u = b (v - w) ; F <- F + (u / s') k^T ; s <- s'.
+// Before s' would leave [2^-40, 2^40] (a zero decay included) F is rescaled to S a, and it
+// is rescaled once at the end.
+constexpr float kFoldScaleMin = 0x1p-40f, kFoldScaleMax = 0x1p40f;
+
+template <int N, int RGW>
+__device__ __forceinline__ void frag_scale(Frag<N, RGW> &F, float x) {
+#pragma unroll
+  for (int i = 0; i < RGW; ++i)
+#pragma unroll
+    for (int f = 0; f < N / 32; ++f) {
+      F.s[i][f].x *= x;
+      F.s[i][f].y *= x;
+      F.s[i][f].z *= x;
+      F.s[i][f].w *= x;
+    }
+}
+
 template <int N, int RGW>
 __device__ __forceinline__ void fold_gdn(Frag<N, RGW> &F, const float *lds, const LdsLayout &L, int nrec, int P, int wave,
                          int lane) {
   const int c = frag_col(lane);
+  float s = 1.f;
   for (int j = 0; j < nrec; ++j) {
     const float al = lds[L.alpha + j], be = lds[L.beta + j];
+    float sn = s * al;
+    if (!(sn >= kFoldScaleMin && sn <= kFoldScaleMax)) {   // the same for every lane (LDS values)
+      frag_scale(F, sn);
+      sn = 1.f;
+    }
     const float *kr = lds + L.K + j * (N + 4) + c;
     float w[RGW];
 #pragma unroll
@@ -968,26 +994,29 @@ __device__ __forceinline__ void fold_gdn(Frag<N, RGW> &F, const float *lds, cons
 #pragma unroll
       for (int i = 0; i < RGW; ++i) w[i] = dot4(F.s[i][f], kf, w[i]);
     }
+    const float inv = 1.f / sn;
     float u[RGW];
 #pragma unroll
     for (int i = 0; i < RGW; ++i) {
       const float wi = oct_sum(w[i]);
       const int row = frag_row(wave, lane, i);
       const float vr = (row < P) ? lds[L.V + j * P + row] : 0.f;
-      u[i] = be * (vr - al * wi);
+      u[i] = be * (vr - sn * wi) * inv;
     }
 #pragma unroll
     for (int f = 0; f < N / 32; ++f) {
       const float4 kf = *(const float4 *)(kr + 32 * f);
 #pragma unroll
       for (int i = 0; i < RGW; ++i) {
-        F.s[i][f].x = fmaf(al, F.s[i][f].x, u[i] * kf.x);
-        F.s[i][f].y = fmaf(al, F.s[i][f].y, u[i] * kf.y);
-        F.s[i][f].z = fmaf(al, F.s[i][f].z, u[i] * kf.z);
-        F.s[i][f].w = fmaf(al, F.s[i][f].w, u[i] * kf.w);
+        F.s[i][f].x = fmaf(u[i], kf.x, F.s[i][f].x);
+        F.s[i][f].y = fmaf(u[i], kf.y, F.s[i][f].y);
+        F.s[i][f].z = fmaf(u[i], kf.z, F.s[i][f].z);
+        F.s[i][f].w = fmaf(u[i], kf.w, F.s[i][f].w);
       }
     }
+    s = sn;
   }
+  if (s != 1.f) frag_scale(F, s);
 }
 
 // KDA fold, one per-channel gated delta-rule update per record in registers:
