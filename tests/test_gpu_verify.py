@@ -9,7 +9,7 @@ from oracle import ReplayOracle
 from synth import accept_counts, decode_inputs, draft_inputs, draft_tree, get_workload, initial_state
 from synth.stream import StepSource
 
-from gpu_util import (TOL, assert_counters, counters, decode, dev, new_state, ptr, relerr, ring_bits,
+from gpu_util import (TOL, assert_counters, check_ring, counters, decode, dev, new_state, ptr, relerr,
                       stream, tile_relerr, to_dev_inputs, verify)
 from oracle_runs import cursor_run, spec_runs
 
@@ -316,7 +316,7 @@ def test_snapshot_commit_errors():
     assert int(err.item()) == R.RSSM_DEVERR_CURSOR
 
 
-def _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=True):
+def _tree_step(ds, orc, wl, s, T, seqs, o, ring=True):
     parent, path, a = draft_tree(wl, s, T)
     dr = draft_inputs(wl, 300 + s, seqs, T)
     d = to_dev_inputs(dr)
@@ -331,16 +331,8 @@ def _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=True):
     _flush(ds, wl.L)
     orc.flush(wl.L)
     assert_counters(ds, orc.n_committed, orc.n_ckpt, f"step {s}")
-    if check_ring:
-        ring = {k: (None if v is None else ring_bits(v)) for k, v in ds.ring_arrays().items()}
-        for i, b in enumerate(seqs):
-            for slot in orc.live_slots(i):
-                assert np.array_equal(ring["alpha"][b, :, slot], orc.ring["alpha"][i, slot])
-                assert np.array_equal(ring["v"][b, :, slot], orc.ring["v"][i, slot])
-                assert np.array_equal(ring["k"][b, :, slot], orc.ring["k"][i, slot])
-                assert np.array_equal(ring["q"][b, :, slot], orc.ring["q"][i, slot])
-                if ring["beta"] is not None:
-                    assert np.array_equal(ring["beta"][b, :, slot], orc.ring["beta"][i, slot])
+    if ring:
+        check_ring(ds, orc, seqs)
     folded = orc.n_ckpt == orc.n_committed
     if folded.any():
         e = tile_relerr(ds.ckpt().cpu().numpy()[folded], orc.S_ckpt[folded]).max()
@@ -509,7 +501,7 @@ def test_tree_spec_full_heads():
     ds = new_state(wl, S0)
     o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
     for s in range(40):
-        _tree_step(ds, orc, wl, s, T, seqs, o, check_ring=(s % 8 == 0))
+        _tree_step(ds, orc, wl, s, T, seqs, o, ring=(s % 8 == 0))
     assert ds.error() == 0
 
 
@@ -670,3 +662,41 @@ def _spec_linear_tree_fused(wl):
         _tree_step(ds, orc, wl, 100 + s, T, seqs, o)
     assert ds.error() == 0
     _fused_loop(wl.replace(L=wl.capacity - 2 * T + 1), 12, tree=False)
+
+
+@pytest.mark.parametrize("name", ["m2_verify_b512", "kda_b256"])
+def test_group_appends_between_speculative_rounds(name):
+    """With 16 value heads the decode appends each group's records from the group's last
+    workgroup.  Decode steps alternate with verify(T) / commit(a) / flush(L) rounds, so those
+    appends land after committed drafts, after folds and at every window phase: every output,
+    cursor and checkpoint against the oracle, and every live ring slot bit for bit."""
+    wl = _small(name, batch=5, n_heads=16, n_qk_heads=16 if name.startswith("m2") else 8)
+    T = wl.t_max
+    seqs = list(range(wl.batch))
+    S0 = initial_state(wl, seqs)
+    orc = ReplayOracle(wl, seqs, S0)
+    ds = new_state(wl, S0)
+    y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
+    o = torch.empty(wl.batch, T, wl.n_heads, wl.dv, device="cuda")
+    for s in range(24):
+        for t in range(2):
+            inp = decode_inputs(wl, 1000 + 2 * s + t, seqs)
+            decode(ds, to_dev_inputs(inp), y)
+            err = relerr(y.cpu().numpy(), orc.decode(inp)).max()
+            assert err <= TOL, f"round {s} decode {t}: rel err {err:.3g}"
+            assert_counters(ds, orc.n_committed, orc.n_ckpt, f"round {s} decode {t}")
+            check_ring(ds, orc, seqs)
+        d = draft_inputs(wl, s, seqs, T)
+        verify(ds, T, to_dev_inputs(d), o)
+        err = relerr(o.cpu().numpy(), orc.verify(d, T)).max()
+        assert err <= TOL, f"round {s}: verify rel err {err:.3g}"
+        acc = accept_counts(wl, s, T)[: wl.batch]
+        _commit(ds, dev(acc), T)
+        orc.commit(acc, T)
+        _flush(ds, wl.L)
+        orc.flush(wl.L)
+        assert_counters(ds, orc.n_committed, orc.n_ckpt, f"round {s} after flush")
+        check_ring(ds, orc, seqs)
+        e = tile_relerr(ds.ckpt().cpu().numpy(), orc.S_ckpt).max()
+        assert e <= TOL, f"round {s}: checkpoint rel err {e:.3g}"
+    assert ds.error() == 0
