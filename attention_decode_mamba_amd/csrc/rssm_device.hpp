@@ -1414,7 +1414,7 @@ __device__ __forceinline__ void widen(const uint4 w, float (&x)[BF ? 8 : 4]) {
 // bounds) and contribute nothing.  The step's record is appended to ring slot
 // (nk + hb) mod C from registers (the input bits).
 template <int N, int RG, int RCF, bool BF>
-__device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG> &RCR, float *wl, int b, int hh,
+__device__ __forceinline__ void m2_nonfold_wave(const Args &a, int tile, float *wl, int b, int hh,
                                                 int gq, int64_t nk, int hb, int lane) {
   const Geom &g = a.g;
   constexpr int es = BF ? 2 : 4, epc = 16 / es;
@@ -1443,7 +1443,7 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
     return (uint32_t)(s >= C ? s - C : s);
   };
 
-  // ---- loads: alpha, query, key rows, value rows (the read copy is in flight already).
+  // ---- loads: alpha, query, key rows, value rows.
   // Records past the window are clamped to the step's input record.
   uint32_t araw;
   {
@@ -1571,7 +1571,10 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
       for (int i = 0; i < CPL; ++i) *(uint4 *)(qd + (kc + R * i) * 16) = qraw[i];
   }
 
-  // ---- S_read q, row sums to LDS (lane c8 of a row writes row group c8's sum)
+  // ---- S_read q, row sums to LDS (lane c8 of a row writes row group c8's sum); the copy is
+  // loaded here, after the record rows are dead
+  RCopy<N, RG> RCR;
+  readcopy_load_rows(RCR, RCF, a.s_read, a.s_read_scale, tile, g.P, lane >> 3, 8, lane);
   float part[RG];
   readcopy_dot(RCR, RCF, wl + W::q, lane, part);
   const int r8 = lane >> 3, c8 = lane & 7;
@@ -1597,9 +1600,10 @@ __device__ __forceinline__ void m2_nonfold_wave(const Args &a, const RCopy<N, RG
 // whole workgroup (see above).  A workgroup takes one value head of 4 consecutive sequences:
 // sequences whose windows are at different positions fold at different steps, so a
 // workgroup rarely has more than one fold to run (4 heads of one sequence would always fold
-// together, and their workgroup would run 4 folds back to back).  The read copy is loaded
-// before the cursor arrives (on a fold step it goes unused).  Requires vector staging, N of
-// 64 or 128, P <= 64 and a window of 2 to 16 records.
+// together, and their workgroup would run 4 folds back to back).  A non-fold wave requests
+// the read copy once its records are consumed: the copy's registers are then never live
+// together with the record rows (fp8: 93 VGPRs instead of 103, 5 waves per SIMD instead of
+// 4).  Requires vector staging, N of 64 or 128, P <= 64 and a window of 2 to 16 records.
 template <int N, int RGW, int RCF, int STG>
 __global__ __launch_bounds__(kThreads) void k_decode_rc(Args a) {
   constexpr bool BF = STG == kStageBf16;
@@ -1615,8 +1619,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_rc(Args a) {
   int *flags = (int *)(lds + decode_rc_flag_offset(g.C + 1, g.P, N, WaveLds<N>::total));
   int fold = 0;
   if (b < g.B) {
-    RCopy<N, RG> RCR;
-    readcopy_load_rows(RCR, RCF, a.s_read, a.s_read_scale, tile, g.P, lane >> 3, 8, lane);
     const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
     const int64_t hb64 = nc - nk;
     if (hb64 < 0 || hb64 > g.C) {
@@ -1624,7 +1626,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_rc(Args a) {
     } else if (hb64 + 1 >= g.L) {
       fold = 1;
     } else {
-      m2_nonfold_wave<N, RG, RCF, BF>(a, RCR, lds + wave * WaveLds<N>::total, b, hh, gq, nk, (int)hb64, lane);
+      m2_nonfold_wave<N, RG, RCF, BF>(a, tile, lds + wave * WaveLds<N>::total, b, hh, gq, nk, (int)hb64, lane);
       if (lane == 0) a.n_committed[tile] = nc + 1;
     }
   }
