@@ -1132,36 +1132,43 @@ __device__ __forceinline__ StageSpec decode_spec(const Args &a, const LdsLayout 
 // ---------------------------------------------------------------- tail appends
 // Small HBM writes cost far more while a launch's read stream runs at full rate than in its
 // last workgroups, when the stream drains.  With H a multiple of 16, the Mamba-2 and KDA
-// decode kernels on the fp32 tile therefore leave the ring appends of each group of 16 value
+// decode kernels on the fp32 tile therefore leave the ring appends of each group of GS value
 // heads of a sequence to the workgroup of the group's last head, and dispatch those
-// workgroups after all others.  That workgroup knows the slot and the fold decision of every
-// head of its group from its own cursor replica, since all replicas of a sequence are equal
-// (a head whose replica disagrees, which only a contract violation can cause, is left out).
-// The appender workgroups carry more work than the others, so the order only pays where the
-// moved writes are large against the end of the grid they lengthen: GDN (smaller records,
-// long delta-rule folds) and the read-copy decode (short non-fold tiles, folds several times
-// longer) keep the appends in each tile's workgroup.
-constexpr int kTailGroup = 16;
+// workgroups after all others.  GS is 16, or 32 for Mamba-2 where H allows it (Mamba-2 with
+// 642-byte records per head ran about 1% faster with 32-head groups; KDA, with 1026-byte
+// records, ran no faster staggered and slower in lockstep).  That workgroup knows the slot
+// and the fold decision of every head of its group from its own cursor replica, since all
+// replicas of a sequence are equal (a head whose replica disagrees, which only a contract
+// violation can cause, is left out).  The appender workgroups carry more work than the
+// others, so the order only pays where the moved writes are large against the end of the
+// grid they lengthen: GDN (smaller records, long delta-rule folds) and the read-copy decode
+// (short non-fold tiles, folds several times longer) keep the appends in each tile's
+// workgroup.
 
+// Heads per group, 0 for appends in each tile's workgroup.
 template <int KIND, int RCF>
-__device__ __forceinline__ bool tail_appends(const Geom &g) {
-  return KIND != RSSM_KIND_GDN && RCF == RSSM_READ_NONE && (g.H % kTailGroup) == 0;
+__device__ __forceinline__ int tail_group(const Geom &g) {
+  if (KIND == RSSM_KIND_GDN || RCF != RSSM_READ_NONE) return 0;
+  if (KIND == RSSM_KIND_MAMBA2 && (g.H % 32) == 0) return 32;
+  return (g.H % 16) == 0 ? 16 : 0;
 }
 
-// Block index -> work item of a grid of `items` whose last 1/16 are the appenders (the
-// groups' last heads): the first 15/16 of the grid takes the items i % 16 != 15 in the
-// XCD-aware order, the rest the items i % 16 == 15.
-__device__ __forceinline__ int tail_item_of_block(int items, bool &appender) {
-  const int na = items / kTailGroup, nm = items - na;
+__device__ __forceinline__ uint64_t tail_full(int gs) { return gs >= 64 ? ~0ull : (1ull << gs) - 1; }
+
+// Block index -> work item of a grid of `items` whose last 1/gs are the appenders (the
+// groups' last heads): the first part of the grid takes the items i % gs != gs - 1 in the
+// XCD-aware order, the rest the items i % gs == gs - 1.
+__device__ __forceinline__ int tail_item_of_block(int items, int gs, bool &appender) {
+  const int na = items / gs, nm = items - na;
   const int bid = blockIdx.x;
   appender = bid >= nm;
   if (!appender) {
     const int i = (nm & 7) == 0 ? (bid & 7) * (nm >> 3) + (bid >> 3) : bid;
-    return (i / (kTailGroup - 1)) * kTailGroup + i % (kTailGroup - 1);
+    return (i / (gs - 1)) * gs + i % (gs - 1);
   }
   const int j = bid - nm;
   const int ai = (na & 7) == 0 ? (j & 7) * (na >> 3) + (j >> 3) : j;
-  return ai * kTailGroup + (kTailGroup - 1);
+  return ai * gs + (gs - 1);
 }
 
 // Copy `bytes` bytes (a multiple of 2) with threads t = 0 .. nthr-1, in the widest pieces
@@ -1178,25 +1185,27 @@ __device__ __forceinline__ void group_copy(uint8_t *__restrict__ dst, const uint
   }
 }
 
-// Bit i set: head h0 + i of sequence b has the appender's counters before this step (nc, nk)
-// or after its own non-fold step (nc + 1, nk).  Its own workgroup may be writing the replica
-// while it is read here, so either value is accepted.  Lanes 0..15 of the calling wave load.
-__device__ __forceinline__ uint32_t tail_group_mask(const Args &a, int b, int h0, int64_t nc, int64_t nk, int lane) {
+// Bit i set: head h0 + i (i < gs <= 64) of sequence b has the appender's counters before
+// this step (nc, nk) or after its own non-fold step (nc + 1, nk).  Its own workgroup may be
+// writing the replica while it is read here, so either value is accepted.  Lane i of the
+// calling wave loads head h0 + i.
+__device__ __forceinline__ uint64_t tail_group_mask(const Args &a, int b, int h0, int gs, int64_t nc, int64_t nk,
+                                                    int lane) {
   bool ok = false;
-  if (lane < kTailGroup) {
+  if (lane < gs) {
     const int tile = b * a.g.H + h0 + lane;
     const int64_t c = __hip_atomic_load(a.n_committed + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int64_t k = __hip_atomic_load(a.n_ckpt + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ok = k == nk && (c == nc || c == nc + 1);
   }
-  return (uint32_t)__ballot(ok) & ((1u << kTailGroup) - 1);
+  return (uint64_t)__ballot(ok) & tail_full(gs);
 }
 
-// Append the step inputs of value heads h0 .. h0+15 of sequence b whose bit is set in `mask`
-// (and the key heads they lead) to ring slot `slot`: byte copies, the ring holding the input
-// dtype.  With every bit set the group's rows are copied as contiguous blocks.
+// Append the step inputs of value heads h0 .. h0+gs-1 of sequence b whose bit is set in
+// `mask` (and the key heads they lead) to ring slot `slot`: byte copies, the ring holding the
+// input dtype.  With every bit set the group's rows are copied as contiguous blocks.
 template <int KIND, int N>
-__device__ void tail_append_group(const Args &a, int b, int h0, int slot, uint32_t mask, int t, int nthr) {
+__device__ void tail_append_group(const Args &a, int b, int h0, int gs, int slot, uint64_t mask, int t, int nthr) {
   const Geom &g = a.g;
   const int64_t es = g.bf16 ? 2 : 4, P = g.P;
   const int64_t na = KIND == RSSM_KIND_KDA ? N : 1;                 // alpha elements per head
@@ -1206,14 +1215,14 @@ __device__ void tail_append_group(const Args &a, int b, int h0, int slot, uint32
   const int64_t kbase = (int64_t)slot * g.B * g.G * N + kin0;       // its ring key row 0
   const uint8_t *iv = (const uint8_t *)a.v, *ia = (const uint8_t *)a.alpha, *ib = (const uint8_t *)a.beta;
   const uint8_t *ik = (const uint8_t *)a.k, *iq = (const uint8_t *)a.q;
-  if (mask == (1u << kTailGroup) - 1) {
+  if (mask == tail_full(gs)) {
     const int ga = (h0 + g.grp - 1) / g.grp;
-    const int gl = (h0 + kTailGroup + g.grp - 1) / g.grp;
+    const int gl = (h0 + gs + g.grp - 1) / g.grp;
     const int gz = gl < g.G ? gl : g.G;                             // key heads [ga, gz) led here
-    group_copy(a.ring + g.off_v + hr * P * es, iv + row0 * P * es, kTailGroup * P * es, t, nthr);
-    group_copy(a.ring + g.off_alpha + hr * na * es, ia + row0 * na * es, kTailGroup * na * es, t, nthr);
+    group_copy(a.ring + g.off_v + hr * P * es, iv + row0 * P * es, gs * P * es, t, nthr);
+    group_copy(a.ring + g.off_alpha + hr * na * es, ia + row0 * na * es, gs * na * es, t, nthr);
     if (KIND != RSSM_KIND_MAMBA2)
-      group_copy(a.ring + g.off_beta + hr * es, ib + row0 * es, kTailGroup * es, t, nthr);
+      group_copy(a.ring + g.off_beta + hr * es, ib + row0 * es, gs * es, t, nthr);
     if (gz > ga) {
       const int64_t ko = (int64_t)ga * N;
       group_copy(a.ring + g.off_k + (kbase + ko) * es, ik + (kin0 + ko) * es, (gz - ga) * N * es, t, nthr);
@@ -1221,7 +1230,7 @@ __device__ void tail_append_group(const Args &a, int b, int h0, int slot, uint32
     }
     return;
   }
-  for (int i = 0; i < kTailGroup; ++i) {
+  for (int i = 0; i < gs; ++i) {
     if (!((mask >> i) & 1)) continue;
     const int h = h0 + i;
     group_copy(a.ring + g.off_v + (hr + i) * P * es, iv + (row0 + i) * P * es, P * es, t, nthr);
@@ -1274,9 +1283,10 @@ __attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) v
   constexpr bool RC = RCF != RSSM_READ_NONE;
   extern __shared__ float lds[];
   const Geom &g = a.g;
-  const bool tail = tail_appends<KIND, RCF>(g);
+  const int gs = tail_group<KIND, RCF>(g);
+  const bool tail = gs > 0;
   bool appender = false;
-  const int tile = tail ? tail_item_of_block(g.B * g.H, appender) : tile_of_block(g.B * g.H);
+  const int tile = tail ? tail_item_of_block(g.B * g.H, gs, appender) : tile_of_block(g.B * g.H);
   const int b = tile / g.H, hh = tile - b * g.H, gq = hh / g.grp;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int64_t nc = a.n_committed[tile], nk = a.n_ckpt[tile];
@@ -1332,14 +1342,14 @@ __attribute__((amdgpu_waves_per_eu(decode_min_waves<KIND, RCF, N, RGW>(), 8))) v
     if (!tail) append_from_lds<KIND, N>(a, L, lds, b, hh, gq, nrec - 1, 0, ring_add(sp.slot0, hb, g.C), t);
   }
   if (appender && !flush) {
-    const int h0 = hh - (kTailGroup - 1);
+    const int h0 = hh - (gs - 1);
     __syncthreads();                                  // every LDS read of the step is done
     if (wave == 0) {
-      const uint32_t m = tail_group_mask(a, b, h0, nc, nk, lane);
-      if (lane == 0) ((uint32_t *)lds)[0] = m;
+      const uint64_t m = tail_group_mask(a, b, h0, gs, nc, nk, lane);
+      if (lane == 0) ((uint64_t *)lds)[0] = m;
     }
     __syncthreads();
-    tail_append_group<KIND, N>(a, b, h0, ring_mod(nc, g.C), ((const uint32_t *)lds)[0], t, kThreads);
+    tail_append_group<KIND, N>(a, b, h0, gs, ring_mod(nc, g.C), ((const uint64_t *)lds)[0], t, kThreads);
   }
   if (t == 0) {
     a.n_committed[tile] = nc + 1;

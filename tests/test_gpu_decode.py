@@ -76,10 +76,10 @@ SHAPES = [
     ("gdn", "fp32", 2, 2, 1, 512, 32, 4, 4),
     ("kda", "bf16", 2, 2, 2, 500, 32, 4, 4),
     ("mamba2", "fp32", 2, 2, 2, 256, 64, 4, 4),
-    # H a multiple of 16: Mamba-2 and KDA append each group of 16 heads from the group's last
-    # workgroup, dispatched after all others (ragged grids; 8 x 16 tiles take the XCD order;
-    # key groups of 8 and of 3 heads; fp32 rows; rows not 16-byte aligned; GDN keeps per-tile
-    # appends)
+    # H a multiple of 16: Mamba-2 and KDA append each group of heads (16; Mamba-2 32 where H
+    # allows) from the group's last workgroup, dispatched after all others (ragged grids; 8 x 16
+    # tiles take the XCD order; key groups of 8 and of 3 heads; fp32 rows; rows not 16-byte
+    # aligned; GDN keeps per-tile appends)
     ("mamba2", "bf16", 3, 16, 16, 16, 32, 4, 4),
     ("mamba2", "bf16", 8, 16, 16, 64, 128, 5, 5),
     ("mamba2", "fp32", 2, 32, 4, 8, 32, 3, 3),
@@ -103,12 +103,12 @@ def test_decode_shapes_and_ragged_tails(shape):
 
 
 @pytest.mark.parametrize("kind,L,H,G", [("mamba2", 4, 3, 3), ("mamba2", 16, 3, 3), ("gdn", 8, 4, 2), ("kda", 8, 4, 2),
-                                         ("mamba2", 8, 16, 16), ("kda", 4, 16, 8)])
+                                         ("mamba2", 8, 16, 16), ("kda", 4, 16, 8), ("mamba2", 6, 32, 32)])
 def test_staggered_windows_decode(kind, L, H, G):
     """Windows at different phases: sequence b first commits b mod L one-draft verifies
     (verify(T=1) + commit(0 or 1)), so each decode step folds only the sequences whose window
     fills on that step.  Every output, cursor and checkpoint against the oracle for 2L steps,
-    and every live ring slot bit for bit (with 16 heads the appends of a sequence's group of 16
+    and every live ring slot bit for bit (with 16 or 32 heads the appends of a sequence's group of
     heads come from its last workgroup, which skips them when the sequence folds)."""
     base = get_workload(_BASE[kind])
     wl = base.replace(name="stagger", batch=2 * L + 1, n_heads=H, n_qk_heads=G, dv=24, dk=64, in_dtype="bf16",
@@ -211,17 +211,17 @@ def test_serving_shape_decode_sampled():
     assert ds.error() == 0
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "kda"])
-def test_decode_cursor_error_with_group_appends(kind):
-    """With 16 value heads the ring appends of a group of 16 heads of a sequence come from the
-    workgroup of its last head.  A broken main tile (1, 2) is left out of its group's appends:
-    its cursors, output rows, checkpoint and ring rows stay untouched, and the rest of sequence
-    1 matches a run without the corruption bit for bit, ring included.  A broken appender
-    (2, 15) sets the error bit and stays untouched; its group's other heads still produce the
-    step's outputs, but their records of that step are not appended.  Sequence 0 matches the
-    clean run bit for bit throughout."""
+@pytest.mark.parametrize("kind,H", [("mamba2", 16), ("mamba2", 32), ("kda", 16), ("kda", 32)])
+def test_decode_cursor_error_with_group_appends(kind, H):
+    """With H a multiple of 16 the ring appends of a group of heads of a sequence (16 heads;
+    Mamba-2 32 where H allows) come from the workgroup of the group's last head.  A broken main tile
+    (1, 2) is left out of its group's appends: its cursors, output rows, checkpoint and ring
+    rows stay untouched, and the rest of sequence 1 matches a run without the corruption bit
+    for bit, ring included.  A broken appender (2, H - 1) sets the error bit and stays
+    untouched; its group's other heads still produce the step's outputs, but their records of
+    that step are not appended.  Sequence 0 matches the clean run bit for bit throughout."""
     base = get_workload("m2_decode_b256" if kind == "mamba2" else "kda_b256")
-    wl = base.replace(name="group_err", batch=3, n_heads=16, n_qk_heads=16, dv=64 if kind == "mamba2" else 32,
+    wl = base.replace(name="group_err", batch=3, n_heads=H, n_qk_heads=H, dv=64 if kind == "mamba2" else 32,
                       dk=128 if kind == "mamba2" else 64, in_dtype="bf16", L=6, capacity=6, t_max=1,
                       read_copy="none")
     seqs = list(range(wl.batch))
@@ -236,8 +236,8 @@ def test_decode_cursor_error_with_group_appends(kind):
         decode(ref, d, y2)
     nc, nk = ds.counters()
     nk[1, 2] = nc[1, 2] + 1                       # h < 0 on a main tile
-    nc[2, 15] = nk[2, 15] + wl.capacity + 1       # h > C on an appender
-    bad = [(1, 2), (2, 15)]
+    nc[2, H - 1] = nk[2, H - 1] + wl.capacity + 1     # h > C on an appender
+    bad = [(1, 2), (2, H - 1)]
     keep_nc, keep_nk = nc.clone(), nk.clone()
     keep_ck = ds.ckpt().clone()
     ring0 = {k: (None if v is None else v.clone()) for k, v in ds.ring_arrays().items()}
@@ -264,7 +264,7 @@ def test_decode_cursor_error_with_group_appends(kind):
         gy, ry = y.cpu()[good], y2.cpu()[good]
         assert torch.equal(gy.view(torch.int32), ry.view(torch.int32)), f"step {t}: healthy outputs differ"
         if t == 3:                                # the group's records up to step 2 were appended
-            assert torch.equal(y[2, :15].cpu().view(torch.int32), y2[2, :15].cpu().view(torch.int32))
+            assert torch.equal(y[2, :H - 1].cpu().view(torch.int32), y2[2, :H - 1].cpu().view(torch.int32))
         rc, rk = ref.counters()
         assert torch.equal(nc.cpu()[good], rc.cpu()[good]) and torch.equal(nk.cpu()[good], rk.cpu()[good])
         assert torch.equal(ds.ckpt().cpu()[good].view(torch.int32), ref.ckpt().cpu()[good].view(torch.int32))
