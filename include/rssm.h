@@ -187,8 +187,9 @@ int rssm_init_state(const rssm_config *cfg, const rssm_state *st, const float *s
  * Then n_committed += 1.
  * Counters out of range on a tile (h < 0 or h > C) set RSSM_DEVERR_CURSOR and leave
  * that tile untouched.  When H is a multiple of 16 (Mamba-2 and KDA without a read
- * copy) the records of each group of 16 value heads of a sequence are appended by the
- * workgroup of the group's last head, late in the launch: a tile whose counters differ
+ * copy) the records of each group of 16 value heads of a sequence (32 for Mamba-2 when H
+ * is a multiple of 32) are appended by the workgroup of the group's last head, late in
+ * the launch: a tile whose counters differ
  * from that head's is left out of the appends, and if the last head's own counters are
  * out of range none of the group's records of this step is appended. */
 int rssm_decode_step(const rssm_config *cfg, const rssm_state *st, const void *alpha,

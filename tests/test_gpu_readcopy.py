@@ -185,8 +185,10 @@ def test_serving_shape_read_copy_sampled(fmt):
 
     Each output row must match the oracle (which quantises its own fp32 checkpoint) to the fp32
     tolerance plus the oracle's bound on what an element lying within that tolerance of a
-    rounding boundary may change; the normwise error is also held to 5e-2 for fp8 and reported
-    for MXFP4, where a single ambiguous E2M1 code moves a row by a few percent."""
+    rounding boundary may change; the normwise error is also held to 5e-2 for fp8 and, for
+    MXFP4, on every row whose allowance is zero (a single ambiguous E2M1 code moves a row by a
+    few percent); the worst MXFP4 error and the share of rows that needed the allowance are
+    reported."""
     wl = get_workload("m2_readcopy_b256").replace(read_copy=fmt)
     steps = 512
     seqs = list(range(wl.batch))
@@ -197,18 +199,31 @@ def test_serving_shape_read_copy_sampled(fmt):
     y = torch.empty(wl.batch, wl.n_heads, wl.dv, device="cuda")
     idx = torch.tensor(sample, device="cuda")
     worst = 0.0
+    worst_plain = 0.0                             # rows whose allowance is zero
     excess = -1.0
+    rows = needed = 0
     with StepSource(wl, seqs) as src:
         for t in range(steps):
             decode(ds, to_dev_inputs(src.decode(t)), y)
             got = y[idx].cpu().numpy()
             for i, b in enumerate(sample):
-                worst = max(worst, relerr(got[i], ref[b]["y"][t]).max())
-                excess = max(excess, read_copy_excess(got[i], ref[b]["y"][t], ref[b]["allowance"][t]).max())
+                yr, allow = ref[b]["y"][t], np.asarray(ref[b]["allowance"][t])
+                err = relerr(got[i], yr)
+                worst = max(worst, err.max())
+                plain = np.broadcast_to(allow, got[i].shape).max(axis=-1) == 0
+                if plain.any():
+                    worst_plain = max(worst_plain, err[plain].max())
+                ex_fp32 = read_copy_excess(got[i], yr, 0.0).max(axis=-1)
+                rows += err.size
+                needed += int((ex_fp32 > 0).sum())
+                excess = max(excess, read_copy_excess(got[i], yr, allow).max())
             if t % 128 == 127:
-                print(f"[read copy {fmt}] step {t + 1}/{steps} worst normwise rel err {worst:.3g}, "
-                      f"worst excess over tolerance+ambiguity {excess:.3g}", flush=True)
+                print(f"[read copy {fmt}] step {t + 1}/{steps} worst normwise rel err {worst:.3g} "
+                      f"({worst_plain:.3g} on rows without allowance), worst excess over "
+                      f"tolerance+ambiguity {excess:.3g}, rows that needed the allowance "
+                      f"{needed}/{rows}", flush=True)
     assert excess <= 0
+    assert worst_plain <= TOL_READ
     if fmt == "fp8":
         assert worst <= TOL_READ
     assert ds.error() == 0
