@@ -125,7 +125,7 @@ def test_read_copy_decode_staggered_windows(fmt, dt, H, G):
     quantisation ambiguity bound; fp8 also normwise); checkpoints bit-identical to the run
     without a copy at every step, and so are a sequence's outputs at its fold steps; cursors;
     every live ring slot bit for bit (also at 16 and 32 heads, where the decode on the fp32
-    tile appends each group of 16 heads from its last workgroup); the final read copy equal to
+    tile appends each group of heads, 16 or 32, from its last workgroup); the final read copy equal to
     the quantised final checkpoint."""
     wl = _wl(fmt, batch=5, n_heads=H, n_qk_heads=G, dv=64, dk=128, in_dtype=dt, L=16, capacity=16, t_max=1)
     seqs = list(range(wl.batch))
